@@ -1,0 +1,208 @@
+"""Benchmark of the fused no-KV-cache attention forward on one MI355X.
+
+One step = one mha_no_cache call over the whole workload (all query tiles,
+all heads, all batches), inputs already resident in HBM. Prints ONE JSON
+line. Default workload: batch 2, 4096 tokens, 32 query heads sharing 8 K/V
+heads, head dim 128, bf16, causal mask, scale 1/sqrt(128).
+
+Metric: attention forward TFLOP/s counting only unmasked (query, key)
+pairs, FLOP = 4 * D * visible_pairs * B * H, and that rate as a fraction of
+MI355X's dense bf16/fp16 MFMA peak (2516.6 TFLOP/s).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+                  [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA, MI355X spec
+METRIC = "attention fwd TFLOP/s (unmasked FLOPs) + % of MFMA bf16 peak, 1×MI355X"
+DEFAULT_WORKLOAD = "gqa_b2_s4096_h32kv8_d128_bf16_causal"
+KERNEL_NAME = "mha_fwd"
+
+
+def visible_pairs(S: int, mask: str, window: int) -> int:
+    """Closed-form count of (query, key) pairs a mask leaves visible in one head."""
+    if mask == "none":
+        return S * S
+    if mask == "causal":
+        return S * (S + 1) // 2
+    w = min(window, S)
+    return S * w - w * (w - 1) // 2
+
+
+def flops(w) -> int:
+    return 4 * w.D * visible_pairs(w.S, w.mask, w.window) * w.B * w.H
+
+
+def algorithmic_bytes(w) -> int:
+    e = 4 if w.dtype == "f32" else 2
+    return e * w.B * w.S * w.D * (2 * w.H + 2 * w.Hkv)  # Q, O, K, V once each
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import head_attention_no_amd as fa
+    from head_attention_no_amd import inputs
+
+    q, k, v = inputs.workload_qkv(w)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sorted(s.elapsed_time(e) for s, e in ev)
+    return {
+        "wall_s": wall,
+        "ms_per_step": wall * 1e3 / steps,
+        "launch_ms_mean": sum(launch_ms) / len(launch_ms),
+        "launch_ms_median": launch_ms[len(launch_ms) // 2],
+        "launch_ms_min": launch_ms[0],
+    }
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample: batch 0, whole K/V head groups
+    (one K/V head and its H/Hkv query heads) until the time budget is spent."""
+    import oracle
+    from head_attention_no_amd import inputs
+
+    q, k, v = inputs.workload_qkv(w)
+    rep = w.H // w.Hkv
+    orc = oracle.default()
+    done, t_total = 0, 0.0
+    for g in range(w.Hkv):
+        qs = q[:1, :, g * rep:(g + 1) * rep].contiguous()
+        ks, vs = k[:1, :, g:g + 1].contiguous(), v[:1, :, g:g + 1].contiguous()
+        t0 = time.perf_counter()
+        orc.attention(qs, ks, vs, w.scale, w.mask, w.window)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    sample_flop = 4 * w.D * visible_pairs(w.S, w.mask, w.window) * rep * done
+    return {
+        "value": sample_flop / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.threads(),
+        "kind": "oracle",
+        "sample": f"batch 0, {done * rep} of {w.B * w.H} (batch, head) pairs "
+                  f"({done} K/V group(s) x {rep} query heads), full S={w.S} rows; "
+                  f"{t_total:.1f} s fp64 on {orc.threads()} threads "
+                  f"({platform.processor() or platform.machine()})",
+        "seconds": t_total,
+    }
+
+
+def roofline(w, t):
+    fl = flops(w)
+    achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": KERNEL_NAME, "flop_per_launch": fl,
+            "launch_ms_mean": round(t["launch_ms_mean"], 5)}
+
+
+def one_line(w, args, t, cpu):
+    fl = flops(w)
+    tflops = fl / (t["ms_per_step"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "Hkv": w.Hkv, "D": w.D,
+                   "mask": w.mask, "window": w.window, "scale": w.scale,
+                   "flop_per_step": fl, "algorithmic_bytes_per_step": algorithmic_bytes(w)},
+        "pct_of_mfma_peak": round(100 * tflops / peak, 2),
+        "roofline": roofline(w, t),
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true",
+                    help="also time the other workloads (reported under 'other_workloads')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the kernel needs no "
+              "collective, and this build measures a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from head_attention_no_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = inputs.BY_NAME[args.workload]
+    print(f"# timing {w.name}: {args.warmup} warmup + {args.steps} steps", file=sys.stderr,
+          flush=True)
+    t = time_gpu(w, args.steps, args.warmup)
+    line = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+    line = one_line(w, args, t, cpu)
+    if args.all:
+        others = {}
+        for o in inputs.WORKLOADS:
+            if o.name == w.name:
+                continue
+            print(f"# timing {o.name}", file=sys.stderr, flush=True)
+            to = time_gpu(o, args.steps, args.warmup)
+            fo = flops(o)
+            others[o.name] = {
+                "ms_per_step": round(to["ms_per_step"], 5),
+                "tflops": round(fo / (to["ms_per_step"] * 1e-3) / 1e12, 2),
+                "launch_ms_mean": round(to["launch_ms_mean"], 5),
+                "pct_of_peak": round(100 * fo / (to["launch_ms_mean"] * 1e-3) / 1e12
+                                     / PEAK_TFLOPS[o.dtype], 2),
+                "peak_tflops": PEAK_TFLOPS[o.dtype],
+            }
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

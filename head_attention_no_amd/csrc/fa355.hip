@@ -1,0 +1,182 @@
+// libfa355: C ABI of the fused no-KV-cache attention forward (see fa355.h).
+//
+// Host side: argument validation (before any HIP call), the gfx950 device
+// check, the choice of kernel instance (dtype x head dim x mask kind) and the
+// launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa355.h"
+#include "mha_fwd_kernel.hpp"
+
+namespace {
+
+using fa355::Params;
+
+const char *const kStatusText[] = {
+    "success",
+    "invalid argument (null pointer, size < 1, H not a multiple of Hkv, unknown dtype or mask, "
+    "window < 1 with the sliding mask, non-finite scale, or out overlapping an input)",
+    "unsupported (head dim other than 64 or 128, pointer not 16-byte aligned, or grid too large)",
+    "no usable device (no current HIP device, or it is not gfx950)",
+    "kernel launch failed",
+};
+
+int elem_size(int dtype) { return dtype == FA355_F32 ? 4 : 2; }
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int block_n(int dtype, int D) { return dtype == FA355_F32 ? 32 : 8192 / D; }
+
+// Shape checks shared by mha_no_cache and fa355_plan.
+int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
+{
+    if (B < 1 || S < 1 || H < 1 || Hkv < 1 || D < 1) return FA355_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA355_ERR_INVALID_ARG;
+    if (dtype != FA355_F32 && dtype != FA355_BF16 && dtype != FA355_F16)
+        return FA355_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA355_ERR_UNSUPPORTED;
+    const int64_t n_qtiles = ((int64_t)S + fa355::kBlockM - 1) / fa355::kBlockM;
+    if (n_qtiles * B * H > INT32_MAX) return FA355_ERR_UNSUPPORTED;
+    return FA355_OK;
+}
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA355_ERR_DEVICE;
+    int state = dev < kMaxDevices ? g_arch_state[dev].load(std::memory_order_relaxed) : 0;
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA355_ERR_DEVICE;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (dev < kMaxDevices) g_arch_state[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? FA355_OK : FA355_ERR_DEVICE;
+}
+
+template <typename T, int D, int MASK>
+hipError_t launch_one(const Params &p, int grid, hipStream_t stream)
+{
+    void *args[] = {const_cast<Params *>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd<T, D, MASK>),
+                           dim3(grid), dim3(fa355::kThreads), args, 0, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_mask(const Params &p, int mask, int grid, hipStream_t stream)
+{
+    switch (mask) {
+    case FA355_MASK_NONE: return launch_one<T, D, fa355::kMaskNone>(p, grid, stream);
+    case FA355_MASK_CAUSAL: return launch_one<T, D, fa355::kMaskCausal>(p, grid, stream);
+    default: return launch_one<T, D, fa355::kMaskWindow>(p, grid, stream);
+    }
+}
+
+template <typename T>
+hipError_t launch_dim(const Params &p, int D, int mask, int grid, hipStream_t stream)
+{
+    return D == 64 ? launch_mask<T, 64>(p, mask, grid, stream)
+                   : launch_mask<T, 128>(p, mask, grid, stream);
+}
+
+}  // namespace
+
+extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void *v, int B, int S,
+                            int H, int Hkv, int D, float scale, int mask_kind, int window,
+                            int dtype, void *stream)
+{
+    // Validation: no HIP call before every argument has been checked.
+    if (!out || !q || !k || !v) return FA355_ERR_INVALID_ARG;
+    int rc = check_shape(B, S, H, Hkv, D, dtype);
+    if (rc == FA355_ERR_INVALID_ARG) return rc;
+    if (mask_kind != FA355_MASK_NONE && mask_kind != FA355_MASK_CAUSAL &&
+        mask_kind != FA355_MASK_SLIDING_WINDOW)
+        return FA355_ERR_INVALID_ARG;
+    if (mask_kind == FA355_MASK_SLIDING_WINDOW && window < 1) return FA355_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA355_ERR_INVALID_ARG;
+    const int64_t es = elem_size(dtype);
+    const int64_t q_bytes = (int64_t)B * S * H * D * es;
+    const int64_t kv_bytes = (int64_t)B * S * Hkv * D * es;
+    if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k, kv_bytes) ||
+        overlaps(out, q_bytes, v, kv_bytes))
+        return FA355_ERR_INVALID_ARG;
+    if (rc != FA355_OK) return rc;
+    if (((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+          reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) &
+         15u) != 0)
+        return FA355_ERR_UNSUPPORTED;
+
+    rc = check_device();
+    if (rc != FA355_OK) return rc;
+
+    Params p;
+    p.out = out;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.B = B;
+    p.S = S;
+    p.H = H;
+    p.Hkv = Hkv;
+    p.rep = H / Hkv;
+    p.n_qtiles = (S + fa355::kBlockM - 1) / fa355::kBlockM;
+    p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
+    // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
+    // goes into Q (an exact bit flip) so the kernel's scale is never negative.
+    p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    const bool neg = std::signbit(scale) && scale != 0.0f;
+    p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
+
+    const int grid = p.n_qtiles * B * H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    switch (dtype) {
+    case FA355_BF16: err = launch_dim<__bf16>(p, D, mask_kind, grid, s); break;
+    case FA355_F16: err = launch_dim<_Float16>(p, D, mask_kind, grid, s); break;
+    default: err = launch_dim<float>(p, D, mask_kind, grid, s); break;
+    }
+    return err == hipSuccess ? FA355_OK : FA355_ERR_LAUNCH;
+}
+
+extern "C" const char *fa355_strerror(int status)
+{
+    if (status < 0 || status > FA355_ERR_LAUNCH) return "unknown status";
+    return kStatusText[status];
+}
+
+extern "C" const char *fa355_version(void) { return "fa355 0.1.0 gfx950"; }
+
+extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups,
+                          int *block_m, int *block_n_out, int *tiles, int n)
+{
+    const int rc = check_shape(B, S, H, Hkv, D, dtype);
+    if (rc != FA355_OK) return rc;
+    const int n_qtiles = (S + fa355::kBlockM - 1) / fa355::kBlockM;
+    const int grid = n_qtiles * B * H;
+    if (num_workgroups) *num_workgroups = grid;
+    if (block_m) *block_m = fa355::kBlockM;
+    if (block_n_out) *block_n_out = block_n(dtype, D);
+    if (tiles) {
+        if (n < 0) return FA355_ERR_INVALID_ARG;
+        for (int w = 0; w < n && w < grid; ++w) {
+            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv);
+            tiles[3 * w + 0] = c.qt;
+            tiles[3 * w + 1] = c.b;
+            tiles[3 * w + 2] = c.h;
+        }
+    }
+    return FA355_OK;
+}

@@ -1,0 +1,130 @@
+/*
+ * libfa355: fused no-KV-cache multi-head attention forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation is mo.mha.no_cache as the "FlashAttentionGPU" API page
+ * (max.modular.com) defines it, section "execute", Steps 0-4:
+ *
+ *     answer = softmax(mask(scale * Q K^T)) V
+ *
+ * with Q, K, V and the answer read and written in BSHD, the BSHD<->BHSD
+ * transposes folded into the kernel's addressing, and the softmax
+ * evaluated as an online (FlashAttention-2) reduction over key tiles, so the
+ * S x S score matrix is never stored.
+ *
+ * C ABI only: plain pointers and sizes, no C++ or framework types. All
+ * functions are thread-safe; the library keeps no per-call state and
+ * allocates no device memory.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out (all four share it). */
+typedef enum {
+    FA355_F32 = 0,  /* IEEE binary32; products and sums in fp32 */
+    FA355_BF16 = 1, /* bfloat16; fp32 accumulation */
+    FA355_F16 = 2   /* IEEE binary16; fp32 accumulation */
+} fa355_dtype;
+
+/*
+ * Mask functor applied to the scaled scores (Step 3 of the page's "execute"
+ * section; the page's mask_str / dispatch_mask selects it). Key j is
+ * visible to query i iff:
+ *   FA355_MASK_NONE:            always;
+ *   FA355_MASK_CAUSAL:          j <= i;
+ *   FA355_MASK_SLIDING_WINDOW:  i - window < j <= i  (the query sees exactly
+ *                               `window` keys, itself included; the page's
+ *                               local_window_size parameter, read as a causal
+ *                               sliding window).
+ * Hidden scores get probability exactly 0.
+ */
+typedef enum {
+    FA355_MASK_NONE = 0,
+    FA355_MASK_CAUSAL = 1,
+    FA355_MASK_SLIDING_WINDOW = 2
+} fa355_mask;
+
+typedef enum {
+    FA355_OK = 0,
+    FA355_ERR_INVALID_ARG = 1, /* bad pointer, size, enum, window or overlap */
+    FA355_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, alignment, size */
+    FA355_ERR_DEVICE = 3,      /* no current HIP device, or it is not gfx950 */
+    FA355_ERR_LAUNCH = 4       /* the HIP launch itself failed */
+} fa355_status;
+
+/*
+ * mha_no_cache: out = softmax(mask(scale * q k^T)) v, per batch and head.
+ *
+ * Arguments (all device pointers on the current HIP device, contiguous):
+ *   out  [B, S, H,   D]  written; same shape and dtype as q ("output ...
+ *                        with the same shape as q", page section "Args").
+ *   q    [B, S, H,   D]  queries, BSHD.
+ *   k    [B, S, Hkv, D]  keys, BSHD, or BShD with Hkv < H for grouped
+ *                        attention (page, grouped attention, "Step -1").
+ *   v    [B, S, Hkv, D]  values, same layout as k ("both key and value
+ *                        must be BShD if one is").
+ *   B, S, H, Hkv, D      batch, sequence length (queries and keys: there is
+ *                        no cache), query heads, K/V heads, head dim.
+ *                        H must be a multiple of Hkv; query head h reads
+ *                        K/V head h / (H / Hkv) (contiguous groups, the
+ *                        reading taken of the page's "G groups").
+ *   scale                multiplies q.k before the mask (page, Step 3);
+ *                        any finite value, 0 and negatives included.
+ *   mask_kind            an fa355_mask value.
+ *   window               sliding-window width (>= 1) for
+ *                        FA355_MASK_SLIDING_WINDOW; ignored otherwise.
+ *   dtype                an fa355_dtype value.
+ *   stream               a hipStream_t, or NULL for the null stream; stands
+ *                        in for the page's DeviceContext.
+ *
+ * Supported today: D in {64, 128}; any S >= 1 (ragged tails are masked);
+ * all three dtypes. Pointers must be 16-byte aligned; out must not overlap
+ * q, k or v. Element offsets are computed in 64 bits.
+ *
+ * Ownership: the caller owns every buffer; the library reads q, k, v and
+ * writes every element of out, and allocates nothing.
+ *
+ * Execution: asynchronous, ordered on `stream`; returns once the kernel is
+ * enqueued. The result is deterministic (no atomics): the same inputs give
+ * the same bits on every run.
+ *
+ * Errors: returns an fa355_status and never aborts. Argument checks run
+ * before any HIP call, so an invalid call touches no device state:
+ * FA355_ERR_INVALID_ARG for a null pointer, a size < 1, H % Hkv != 0, an
+ * unknown dtype or mask, window < 1 with the sliding mask, a non-finite
+ * scale, or out overlapping an input; FA355_ERR_UNSUPPORTED for another D,
+ * a misaligned pointer or a grid too large to launch; FA355_ERR_DEVICE if
+ * no HIP device is current or it is not gfx950; FA355_ERR_LAUNCH if the
+ * launch fails.
+ */
+int mha_no_cache(void *out, const void *q, const void *k, const void *v, int B, int S, int H,
+                 int Hkv, int D, float scale, int mask_kind, int window, int dtype, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *fa355_strerror(int status);
+
+/* Library version string, e.g. "fa355 0.1.0 gfx950". */
+const char *fa355_version(void);
+
+/*
+ * Work decomposition of one mha_no_cache call, for inspection and tests;
+ * pure host arithmetic, no HIP call. Given the call's shape, reports the
+ * number of workgroups and, for each of the first `n` workgroup indices,
+ * which (query tile, batch, head) it computes: tiles[3*w + 0] = query tile
+ * (rows tile*block_m ... tile*block_m + block_m - 1), tiles[3*w + 1] = b,
+ * tiles[3*w + 2] = h. `tiles` may be NULL to query only the sizes.
+ * Returns FA355_OK or FA355_ERR_INVALID_ARG / FA355_ERR_UNSUPPORTED under
+ * the same rules as mha_no_cache.
+ */
+int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups, int *block_m,
+               int *block_n, int *tiles, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -96,6 +96,8 @@ class Oracle:
         lib.fa355_oracle_probs.restype = i
         lib.fa355_oracle_visible_pairs.argtypes = [i, i, i]
         lib.fa355_oracle_visible_pairs.restype = ctypes.c_int64
+        lib.fa355_oracle_threads.argtypes = []
+        lib.fa355_oracle_threads.restype = i
         self.lib = lib
         self.path = path
 
@@ -138,6 +140,10 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected the arguments (status {rc})")
         return p
+
+    def threads(self) -> int:
+        """Number of threads the oracle's parallel loops use."""
+        return int(self.lib.fa355_oracle_threads())
 
     def visible_pairs(self, S: int, mask, window: int = -1) -> int:
         """Count of (query, key) pairs the mask leaves visible in one head."""

@@ -249,3 +249,13 @@ int64_t fa355_oracle_visible_pairs(int S, int mask_kind, int window)
             n += visible(mask_kind, window, i, j);
     return n;
 }
+
+/* Threads an OpenMP region of this library would use (1 without OpenMP). */
+int fa355_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports what fa355.h declares, and
+rejects bad arguments before touching HIP. No compute call runs here."""
+import os
+import re
+
+import pytest
+
+import head_attention_no_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+# Fake, never-dereferenced addresses: every call below fails validation first.
+P1, P2, P3, P4 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(fa.EXPORTS), names
+    lib = fa.load()
+    for n in names:
+        assert hasattr(lib, n), f"libfa355.so does not export {n}"
+
+
+def test_version_and_strerror():
+    assert fa.version().startswith("fa355 ")
+    for s in range(5):
+        assert fa.strerror(s)
+    assert fa.strerror(99) == "unknown status"
+
+
+def call(**over):
+    a = dict(out=P1, q=P2, k=P3, v=P4, B=1, S=128, H=4, Hkv=4, D=64, scale=0.125,
+             mask_kind=fa.MASK_NONE, window=-1, dtype=fa.BF16, stream=None)
+    a.update(over)
+    return fa.mha_no_cache(a["out"], a["q"], a["k"], a["v"], a["B"], a["S"], a["H"], a["Hkv"],
+                           a["D"], a["scale"], a["mask_kind"], a["window"], a["dtype"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(out=None), dict(q=None), dict(k=None), dict(v=None),
+    dict(B=0), dict(S=0), dict(H=0), dict(Hkv=0), dict(D=0), dict(S=-5),
+    dict(H=4, Hkv=3), dict(H=2, Hkv=4),
+    dict(dtype=3), dict(dtype=-1), dict(mask_kind=3), dict(mask_kind=-1),
+    dict(mask_kind=fa.MASK_SLIDING_WINDOW, window=0),
+    dict(mask_kind=fa.MASK_SLIDING_WINDOW, window=-1),
+    dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(out=P2 + 64),                 # out overlaps q
+    dict(out=P3 - 32),                 # out runs into k
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_invalid_arguments(over):
+    assert call(**over) == fa.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over", [
+    dict(D=32), dict(D=96), dict(D=256),
+    dict(q=P2 + 2), dict(out=P1 + 8), dict(k=P3 + 4), dict(v=P4 + 1),
+    dict(B=1 << 12, S=1 << 17, H=1 << 10, Hkv=1 << 10, out=1 << 47, q=2 << 47, k=3 << 47,
+         v=4 << 47),                  # 2^32 workgroups
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_unsupported_arguments(over):
+    assert call(**over) == fa.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 4096, 32, 8, 128, fa.BF16),   # (batch, K/V head) groups split over the 8 XCDs
+    (4, 2048, 32, 32, 128, fa.BF16),
+    (1, 8192, 32, 8, 128, fa.BF16),
+    (1, 16384, 16, 16, 64, fa.F16),
+    (1, 128, 4, 4, 64, fa.F32),       # 4 groups: fallback order
+    (3, 300, 6, 2, 64, fa.BF16),      # ragged S, 6 groups
+    (1, 1, 1, 1, 128, fa.F16),
+])
+def test_plan_covers_every_tile_once(shape):
+    B, S, H, Hkv, D, dt = shape
+    pl = fa.plan(B, S, H, Hkv, D, dt, with_tiles=True)
+    nq = -(-S // pl["block_m"])
+    assert pl["block_m"] == 128
+    assert pl["block_n"] == (32 if dt == fa.F32 else 8192 // D)
+    assert pl["num_workgroups"] == nq * B * H
+    tiles = pl["tiles"]
+    assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B) for h in range(H))
+    # Longest (last) query tiles are dispatched first.
+    first = tiles[:min(len(tiles), B * H)]
+    assert all(t == nq - 1 for t, _, _ in first)
+
+
+def test_plan_keeps_shared_kv_heads_on_one_xcd():
+    B, S, H, Hkv = 2, 4096, 32, 8
+    tiles = fa.plan(B, S, H, Hkv, 128, fa.BF16, with_tiles=True)["tiles"]
+    xcd_of_group = {}
+    for w, (_, b, h) in enumerate(tiles):
+        grp = (b, h // (H // Hkv))
+        xcd_of_group.setdefault(grp, set()).add(w % 8)
+    assert all(len(x) == 1 for x in xcd_of_group.values())
+    # every XCD receives the same number of groups
+    counts = {}
+    for x in xcd_of_group.values():
+        counts[next(iter(x))] = counts.get(next(iter(x)), 0) + 1
+    assert sorted(counts) == list(range(8)) and len(set(counts.values())) == 1
+
+
+def test_plan_rejects_like_the_entry_point():
+    with pytest.raises(fa.FA355Error):
+        fa.plan(1, 128, 4, 3, 64, fa.BF16)
+    with pytest.raises(fa.FA355Error):
+        fa.plan(1, 128, 4, 4, 48, fa.BF16)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load(str(tmp_path / "libfa355.so"))

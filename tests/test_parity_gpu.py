@@ -1,0 +1,221 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Tolerances (against the fp64 oracle on the same rounded inputs):
+  fp32 inputs:       max |err| <= 1e-4
+  bf16/fp16 inputs:  max |err| <= 2e-2 and mean |err| <= 2e-3
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_no_amd as fa
+import oracle
+from head_attention_no_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2e-3), "f16": (2e-2, 2e-3)}
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(q, k, v, scale, mask, window):
+    out = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), scale, mask, window)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def check(got, want, dtype, what):
+    got = got.to(torch.float64).numpy()
+    err = np.abs(got - want)
+    mx_tol, mean_tol = TOL[dtype]
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= mx_tol, f"{what}: max err {err.max():.3e} at {worst}"
+    assert err.mean() <= mean_tol, f"{what}: mean err {err.mean():.3e}"
+    return err.max(), err.mean()
+
+
+SMALL = [
+    # B, S, H, Hkv, D, dtype, mask, window
+    (1, 128, 4, 4, 64, "f32", "none", -1),
+    (1, 1, 2, 1, 64, "bf16", "causal", -1),
+    (1, 1, 1, 1, 128, "f16", "none", -1),
+    (2, 37, 4, 2, 64, "bf16", "none", -1),
+    (1, 200, 4, 4, 128, "bf16", "causal", -1),
+    (2, 300, 6, 2, 128, "bf16", "causal", -1),
+    (1, 300, 8, 1, 128, "f16", "causal", -1),
+    (1, 257, 4, 4, 64, "f16", "none", -1),
+    (1, 513, 4, 2, 64, "bf16", "causal", -1),
+    (1, 300, 4, 2, 128, "bf16", "sliding_window", 1),
+    (1, 300, 4, 2, 128, "bf16", "sliding_window", 17),
+    (1, 400, 4, 1, 128, "bf16", "sliding_window", 100),
+    (1, 390, 4, 4, 64, "f16", "sliding_window", 129),
+    (1, 300, 4, 4, 128, "f16", "sliding_window", 5000),
+    (1, 300, 4, 2, 128, "f32", "none", -1),
+    (1, 300, 4, 2, 128, "f32", "causal", -1),
+    (1, 275, 4, 4, 64, "f32", "sliding_window", 40),
+    (2, 160, 4, 2, 64, "f32", "causal", -1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}_S{}_H{}kv{}_D{}_{}_{}_W{}".format(*c))
+def test_small_whole_output(case):
+    B, S, H, Hkv, D, dt, mask, window = case
+    seed = 7 + S + 3 * H + D
+    note(f"case {case} seed {seed}")
+    q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed)
+    scale = 1.0 / math.sqrt(D)
+    got = run_gpu(q, k, v, scale, mask, window)
+    want = oracle.attention(q, k, v, scale, mask, window)
+    check(got, want, dt, str(case))
+
+
+def test_workload_small_fp32_whole_output():
+    w = inputs.WORKLOADS[0]
+    note(f"workload {w.name}")
+    q, k, v = inputs.workload_qkv(w)
+    got = run_gpu(q, k, v, w.scale, w.mask, w.window)
+    want = oracle.attention(q, k, v, w.scale, w.mask, w.window)
+    mx, mean = check(got, want, w.dtype, w.name)
+    note(f"  max {mx:.3e} mean {mean:.3e}")
+
+
+def sample_rows(w, n_heads=6, seed=0):
+    """(b, h, i) triples: tile edges, both ends, and random rows of a few heads."""
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < min(n_heads, w.B * w.H):
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, 129, w.S // 2, w.S - 129, w.S - 128, w.S - 2, w.S - 1}
+    rows = []
+    for b, h in sorted(heads):
+        idx = sorted({i for i in fixed if 0 <= i < w.S} | set(rng.integers(0, w.S, 24).tolist()))
+        rows += [(b, h, i) for i in idx]
+    return rows
+
+
+@pytest.mark.parametrize("w", inputs.WORKLOADS[1:], ids=lambda w: w.name)
+def test_workload_full_size_sampled_rows(w):
+    """Full-size workloads, launched exactly as the benchmark launches them;
+    the oracle recomputes a sample of rows one by one."""
+    note(f"workload {w.name}")
+    q, k, v = inputs.workload_qkv(w)
+    got = run_gpu(q, k, v, w.scale, w.mask, w.window)
+    assert torch.isfinite(got.float()).all()
+    rows = sample_rows(w)
+    want = oracle.attention_rows(q, k, v, w.scale, w.mask, w.window, rows)
+    got_rows = torch.stack([got[b, i, h] for b, h, i in rows])
+    mx, mean = check(got_rows, want, w.dtype, w.name)
+    note(f"  {len(rows)} rows: max {mx:.3e} mean {mean:.3e}")
+
+
+def _dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mask,window", [("none", -1), ("causal", -1), ("sliding_window", 33)])
+def test_values_one_give_one(dt, mask, window):
+    q, k, v = inputs.make_qkv(1, 300, 4, 2, 128, dt, seed=3)
+    note(f"V=1 {dt} {mask}")
+    q, k, v = _dev(q, k, torch.ones_like(v))
+    out = fa.attention(q, k, v, 0.2, mask, window).float()
+    assert torch.allclose(out, torch.ones_like(out), atol=TOL[dt][0], rtol=0)
+
+
+@pytest.mark.parametrize("mask,window", [("none", -1), ("causal", -1), ("sliding_window", 70)])
+def test_scale_zero_is_mean_of_visible_values(mask, window):
+    q, k, v = inputs.make_qkv(2, 333, 4, 2, 64, "f32", seed=4)
+    note(f"scale=0 {mask}")
+    got = run_gpu(q, k, v, 0.0, mask, window)
+    want = oracle.attention(q, k, v, 0.0, mask, window)
+    check(got, want, "f32", f"scale 0 {mask}")
+
+
+def test_negative_scale():
+    q, k, v = inputs.make_qkv(1, 260, 4, 2, 128, "bf16", seed=5)
+    got = run_gpu(q, k, v, -0.3, "causal", -1)
+    check(got, oracle.attention(q, k, v, -0.3, "causal", -1), "bf16", "negative scale")
+
+
+def test_mask_special_cases():
+    q, k, v = inputs.make_qkv(1, 300, 4, 2, 128, "bf16", seed=6)
+    qd, kd, vd = _dev(q, k, v)
+    causal = fa.attention(qd, kd, vd, 0.1, "causal").cpu()
+    assert torch.equal(causal[:, 0], v[:, 0].repeat_interleave(2, dim=1))
+    w1 = fa.attention(qd, kd, vd, 0.1, "sliding_window", 1).cpu()
+    assert torch.equal(w1, v.repeat_interleave(2, dim=2))
+    for W in (300, 301, 10 ** 6):
+        wide = fa.attention(qd, kd, vd, 0.1, "sliding_window", W).cpu()
+        assert torch.equal(wide, causal), f"window {W} must equal causal"
+
+
+@pytest.mark.parametrize("mask,window", [("none", -1), ("causal", -1), ("sliding_window", 50)])
+def test_grouped_equals_repeated_heads(mask, window):
+    q, k, v = inputs.make_qkv(2, 200, 8, 2, 128, "bf16", seed=8)
+    qd, kd, vd = _dev(q, k, v)
+    grouped = fa.attention(qd, kd, vd, 0.1, mask, window)
+    rep = fa.attention(qd, kd.repeat_interleave(4, dim=2).contiguous(),
+                       vd.repeat_interleave(4, dim=2).contiguous(), 0.1, mask, window)
+    assert torch.equal(grouped, rep)
+
+
+def test_key_shift_invariance_fp32():
+    """A constant vector added to every key shifts each score row by a
+    constant (here several hundred), which the running max must absorb."""
+    q, k, v = inputs.make_qkv(1, 260, 2, 2, 64, "f32", seed=9)
+    u = torch.randn(64, generator=torch.Generator().manual_seed(1)) * 60.0
+    got = run_gpu(q, k + u, v, 1.0 / 8, "causal", -1)
+    want = oracle.attention(q, k, v, 1.0 / 8, "causal", -1)
+    check(got, want, "f32", "key shift")
+
+
+def test_peaky_softmax_fp16_small():
+    w = inputs.WORKLOADS[4].with_(S=640, H=4, Hkv=4)
+    q, k, v = inputs.workload_qkv(w)
+    got = run_gpu(q, k, v, w.scale, w.mask, w.window)
+    check(got, oracle.attention(q, k, v, w.scale, w.mask, w.window), "f16", "peaky fp16")
+
+
+def test_deterministic_and_writes_every_element():
+    q, k, v = inputs.make_qkv(2, 333, 8, 2, 128, "bf16", seed=10)
+    qd, kd, vd = _dev(q, k, v)
+    n = q.numel()
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    guard = torch.arange(2048, device=DEV).to(torch.bfloat16)
+    buf[:2048] = guard
+    buf[-2048:] = guard
+    out = buf[2048:2048 + n].view(q.shape)
+    fa.attention(qd, kd, vd, 0.09, "causal", out=out)
+    first = out.clone()
+    fa.attention(qd, kd, vd, 0.09, "causal", out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(first.float()).any(), "some output element was never written"
+    assert torch.equal(first, out), "two runs differ"
+    assert torch.equal(buf[:2048], guard) and torch.equal(buf[-2048:], guard), "write out of bounds"
+
+
+def test_side_stream():
+    q, k, v = inputs.make_qkv(1, 256, 4, 4, 64, "f16", seed=11)
+    qd, kd, vd = _dev(q, k, v)
+    ref = fa.attention(qd, kd, vd, 0.125, "causal")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = fa.attention(qd, kd, vd, 0.125, "causal")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_rejects_through_binding():
+    q, k, v = inputs.make_qkv(1, 64, 4, 3, 64, "bf16", seed=12)
+    with pytest.raises(fa.FA355Error) as e:
+        fa.attention(*_dev(q, k, v), 0.1, "none")
+    assert e.value.status == fa.ERR_INVALID_ARG
