@@ -116,6 +116,28 @@ def cpu_baseline(w, budget_s: float = 12.0):
     }
 
 
+def copy_calibration(mib: int, steps: int, warmup: int):
+    """A plain device-to-device copy of known size: its HBM counters per
+    dispatch calibrate the ones read for the attention kernel."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
+            "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}
+
+
 def roofline(w, t):
     fl = flops(w)
     achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -161,6 +183,9 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (reported under 'other_workloads')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead, time a plain device copy of MIB MiB (reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the kernel needs no "
@@ -174,6 +199,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.copy_calibration, args.steps, args.warmup)))
+        return
     w = inputs.BY_NAME[args.workload]
     print(f"# timing {w.name}: {args.warmup} warmup + {args.steps} steps", file=sys.stderr,
           flush=True)

@@ -9,9 +9,11 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "fa355.h"
-#include "mha_fwd_kernel.hpp"
+#include "mha_fwd16.hpp"
+#include "mha_fwd32.hpp"
 
 namespace {
 
@@ -21,7 +23,7 @@ const char *const kStatusText[] = {
     "success",
     "invalid argument (null pointer, size < 1, H not a multiple of Hkv, unknown dtype or mask, "
     "window < 1 with the sliding mask, non-finite scale, or out overlapping an input)",
-    "unsupported (head dim other than 64 or 128, pointer not 16-byte aligned, or grid too large)",
+    "unsupported (head dim other than 64 or 128, pointer not 16-byte aligned, grid too large, or one K/V head slice of 2 GiB or more)",
     "no usable device (no current HIP device, or it is not gfx950)",
     "kernel launch failed",
 };
@@ -46,6 +48,9 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     if (D != 64 && D != 128) return FA355_ERR_UNSUPPORTED;
     const int64_t n_qtiles = ((int64_t)S + fa355::kBlockM - 1) / fa355::kBlockM;
     if (n_qtiles * B * H > INT32_MAX) return FA355_ERR_UNSUPPORTED;
+    // The 16-bit kernel addresses one (batch, K/V head) slice with 32-bit
+    // byte offsets: S rows of Hkv * D elements must stay below 2 GiB.
+    if ((int64_t)S * Hkv * D * elem_size(dtype) >= ((int64_t)1 << 31)) return FA355_ERR_UNSUPPORTED;
     return FA355_OK;
 }
 
@@ -71,8 +76,12 @@ template <typename T, int D, int MASK>
 hipError_t launch_one(const Params &p, int grid, hipStream_t stream)
 {
     void *args[] = {const_cast<Params *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd<T, D, MASK>),
-                           dim3(grid), dim3(fa355::kThreads), args, 0, stream);
+    const void *fn;
+    if constexpr (std::is_same_v<T, float>)
+        fn = reinterpret_cast<const void *>(&fa355::mha_fwd32<D, MASK>);
+    else
+        fn = reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(fa355::kThreads), args, 0, stream);
 }
 
 template <typename T, int D>

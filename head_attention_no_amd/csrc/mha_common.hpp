@@ -1,0 +1,216 @@
+// Shared pieces of the gfx950 attention-forward kernels: kernel arguments,
+// the workgroup -> tile map, masks and small device helpers.
+//
+// The operation is the no-KV-cache attention of the "FlashAttentionGPU" API
+// page (max.modular.com, section "execute", Steps 0-4):
+// answer = softmax(mask(scale * Q K^T)) V per (batch, head), BSHD in and out,
+// K/V heads shared by H/Hkv consecutive query heads (grouped attention).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace fa355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+
+// Kernel arguments (one struct, passed by value).
+struct Params {
+    void *out;
+    const void *q;
+    const void *k;
+    const void *v;
+    int B, S, H, Hkv;
+    int rep;       // H / Hkv: query heads per K/V head
+    int n_qtiles;  // ceil(S / kBlockM)
+    int window;    // sliding-window width, clamped to S (a window >= S is causal)
+    float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
+    uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|
+};
+
+constexpr int kThreads = 256;  // 4 waves of 64 lanes
+constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
+
+// Lazy rescaling: the running max is only raised when a new tile's max
+// exceeds it by more than this many powers of two, so P stays <= 2^8 and
+// most tiles skip the O rescale altogether.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Workgroup -> (query tile, batch, head). Hardware dispatches workgroup w to
+// XCD w % 8 as that XCD's (w / 8)-th workgroup. When the (batch, K/V head)
+// groups split evenly over the 8 XCDs, every XCD gets whole groups (so the
+// H/Hkv query heads that share K/V also share that XCD's L2) and the same
+// mix of tile lengths; within an XCD, and in the fallback order, the longest
+// query tiles (the last ones, under a causal mask) start first.
+struct TileCoord {
+    int qt, b, h;
+};
+
+__host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv)
+{
+    const int rep = H / Hkv;
+    const int groups = B * Hkv;
+    TileCoord c;
+    if (groups % 8 == 0) {
+        const int x = w % 8, slot = w / 8;
+        const int per_tile = (groups / 8) * rep;
+        const int qi = slot / per_tile;
+        const int rem = slot % per_tile;
+        const int grp = (rem / rep) * 8 + x;
+        c.b = grp / Hkv;
+        c.h = (grp % Hkv) * rep + rem % rep;
+        c.qt = n_qtiles - 1 - qi;
+    } else {
+        const int bh = B * H;
+        c.qt = n_qtiles - 1 - w / bh;
+        c.b = (w % bh) / H;
+        c.h = w % H;
+    }
+    return c;
+}
+
+// Tile classification for one wave's 32 rows [r0, r0+31] and keys [k0, k1].
+enum TileClass { kEmpty = 0, kFull = 1, kEdge = 2 };
+
+template <int MASK>
+__device__ inline int classify(int r0, int k0, int k1, int S, int W)
+{
+    if (r0 >= S) return kEmpty;  // padding rows only
+    const int r1 = r0 + 31;
+    const bool tail = k1 >= S;
+    if (MASK == kMaskNone) return tail ? kEdge : kFull;
+    if (k0 > r1) return kEmpty;
+    if (MASK == kMaskWindow && k1 <= r0 - W) return kEmpty;
+    bool full = k1 <= r0 && !tail;
+    if (MASK == kMaskWindow) full = full && k0 > r1 - W;
+    return full ? kFull : kEdge;
+}
+
+// The mask functor plus the end of the sequence: may query `row` see `key`?
+template <int MASK>
+__device__ inline bool visible(int row, int key, int S, int W)
+{
+    if (key >= S) return false;
+    if (MASK == kMaskNone) return true;
+    if (key > row) return false;
+    if (MASK == kMaskWindow) return key > row - W;
+    return true;
+}
+
+// Key-tile range [begin, end) a workgroup whose first row is q0 must visit.
+template <int MASK, int BN>
+__device__ inline void key_tile_range(int q0, int S, int W, int &begin, int &end)
+{
+    const int q_last = min(q0 + kBlockM, S) - 1;
+    begin = 0;
+    end = (S + BN - 1) / BN;
+    if (MASK != kMaskNone) end = min(end, q_last / BN + 1);
+    if (MASK == kMaskWindow) begin = max(0, q0 - W + 1) / BN;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F &f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_from<0, N>(f);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a per-lane value with the one held by lane ^ 32 (the other half of
+// the same query row): returns op(x[lane], x[lane ^ 32]) in every lane.
+__device__ inline float half_max(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ inline float half_sum(float x)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ inline bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Round 2 floats to a packed pair of 16-bit values (round to nearest even).
+template <typename T>
+__device__ inline uint32_t pack2(float a, float b);
+
+template <>
+__device__ inline uint32_t pack2<__bf16>(float a, float b)
+{
+    f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+template <>
+__device__ inline uint32_t pack2<_Float16>(float a, float b)
+{
+    f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+// acc + lo(x) + hi(x) for a packed pair of 16-bit values, in fp32.
+template <typename T>
+__device__ inline float sum2(uint32_t x, float acc);
+
+template <>
+__device__ inline float sum2<__bf16>(uint32_t x, float acc)
+{
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
+
+template <>
+__device__ inline float sum2<_Float16>(uint32_t x, float acc)
+{
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+}
+
+// D = A B + C on a 32x32x16 16-bit MFMA (A: 32 rows x 16 k, B: 16 k x 32 cols).
+template <typename T>
+__device__ inline f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ inline f32x16 mfma16<__bf16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ inline f32x16 mfma16<_Float16>(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline u32x4 ldg16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+}  // namespace fa355

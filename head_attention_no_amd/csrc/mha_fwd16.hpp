@@ -1,0 +1,345 @@
+// bf16 / fp16 attention forward for gfx950 (MI355X).
+//
+// Online-softmax (FlashAttention-2) reduction over key tiles: the
+// "Optimizing attention via FlashAttention" section of the recipe page
+// "Custom Operations: Applications in AI Models" and tiny_flash_attn.py's
+// flash_attn_v2 keep a running row max m and row sum l per query, rescale
+// the output by exp(m_old - m_new) and divide by l once after the last key
+// tile. Scale and mask are applied to the scores before the softmax, as the
+// "FlashAttentionGPU" API page (section "execute", Step 3) specifies.
+//
+// Decomposition: one 4-wave workgroup per (query tile of 128 rows, batch,
+// head); each wave owns 32 query rows; key tiles of BN = 8192 / D keys.
+//
+// Register layouts (32x32x16 MFMA; lane = 0..63, c = lane % 32, g = lane / 32):
+//  * Scores are computed transposed, S^T = K Q^T, so the accumulator column
+//    is the query row: lane (c, g) holds, for 32-key sub-tile t,
+//    S^T[key = 32t + 8i + 4g + j][query c] in element 4i + j. A query row
+//    lives in two lanes (c and c + 32); its max needs one v_permlane32_swap
+//    per key tile and its sum one at the very end.
+//  * Q is the B operand (k-step s: Q[c][16s + 8g .. +7]) and stays in
+//    registers for the whole key loop.
+//  * P^T is used in place as the B operand of O^T = V^T P^T: for PV k-step
+//    s the 8 values are accumulator elements 8(s%2) .. 8(s%2)+7 of sub-tile
+//    s/2, i.e. keys 16s + 8(e/4) + 4g + e%4 (e = 0..7). The V^T A operand is
+//    read with the transposing LDS load ds_read_b64_tr_b16, two per
+//    operand, which delivers exactly that key order (see below).
+//  * O^T accumulates in fp32: lane (c, g) holds O[query c][d = 32t + 8i + 4g + j].
+//
+// K/V staging: buffer_load_dwordx4 ... lds copies 16-byte pieces straight
+// from global memory into LDS (lane l of a copy lands at byte 16 l of a
+// 1 KiB block), double buffered, with no register staging. A 1 KiB block
+// holds one key group of G = 512 / D keys (4 or 8) in full, as 16-byte
+// slots ordered [chunk][key in group]:
+//    K: slot = (chunk ^ swK(group)) * G + key%G
+//    V: slot = chunk * G + (key%G ^ swV(chunk))
+// The XOR swizzles make the 16 lanes that share a bank cycle read distinct
+// banks, and keep every read address of a tile an immediate offset from one
+// per-lane base. Rows past the end of the sequence fall outside the buffer
+// resource's range and read as zero.
+//
+// ds_read_b64_tr_b16, per 16-lane group: lane i receives element i%4 of the
+// 8 bytes addressed by lane 4k + i/4, for k = 0..3. Lane 16q + j addresses
+// V[key 4(q/2) + j/4 (+16s, +8 for the second half)][d 16(q%2) + 4(j%4)
+// (+32t) .. +3], so lane (c, g) receives V[16s + 4g + k (+8)][32t + c].
+//
+// Masking: key tiles wholly hidden from a wave are skipped (the workgroup
+// only copies tiles some of its rows can see); tiles wholly visible run
+// without any per-element test; only edge tiles (the diagonal, the window's
+// far edge, the ragged end of the sequence) test each element.
+#pragma once
+
+#include "mha_common.hpp"
+
+namespace fa355 {
+
+// Word 3 of a raw buffer resource (untyped 32-bit access, range checked).
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int D>
+struct Tile16 {
+    static constexpr int BN = 8192 / D;           // keys per tile (64 or 128)
+    static constexpr int NKT = BN / 32;           // 32-key sub-tiles of S^T
+    static constexpr int ND = D / 32;             // 32-dim sub-tiles of O^T
+    static constexpr int G = 512 / D;             // keys per 1 KiB key group
+    static constexpr int TILE_BYTES = BN * D * 2;  // 16 KiB
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile, then V tile
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered
+    static constexpr int GROUPS = BN / G;         // key groups per tile
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(GROUPS == 16, "4 waves x 4 key groups of K and of V per tile");
+};
+
+template <int D>
+__device__ inline int k_swz(int kg) { return kg & (D == 128 ? 3 : 1); }
+template <int D>
+__device__ inline int v_swz(int chunk) { return D == 128 ? 0 : 4 * ((chunk >> 1) & 1); }
+
+// Byte offsets of K[key][16-byte chunk c] and V[key][c] inside a tile region.
+template <int D>
+__device__ inline int k_lds_offset(int key, int c)
+{
+    constexpr int G = Tile16<D>::G;
+    const int kg = key / G;
+    return kg * 1024 + ((c ^ k_swz<D>(kg)) * G + key % G) * 16;
+}
+template <int D>
+__device__ inline int v_lds_offset(int key, int c)
+{
+    constexpr int G = Tile16<D>::G;
+    return (key / G) * 1024 + (c * G + ((key % G) ^ v_swz<D>(c))) * 16;
+}
+
+// Transposing LDS read at byte address addr + OFF (see the layout note above).
+// Written as inline asm: the compiler cannot tell this read apart from the
+// in-flight global -> LDS copies of the next tile and would otherwise wait
+// for them before every such read. The ordering it would enforce is already
+// explicit (copies are waited for and barriered before a tile is read), so
+// only the read's own completion is needed: lds_wait() below.
+template <int OFF>
+__device__ inline u32x2 lds_read_tr16(uint32_t addr)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+
+// Wait until every LDS read this wave issued has returned, and make the
+// registers in `r` depend on that wait.
+template <int N>
+__device__ inline void lds_wait(u32x2 (&r)[N])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+__device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds_dst, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_dst,
+                                             16, voffset, 0, 0, 0);
+}
+
+// Wait for this wave's outstanding global -> LDS copies (vmcnt = 0).
+__device__ inline void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <typename T, int D, int MASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mha_fwd16(Params p)
+{
+    using TL = Tile16<D>;
+    constexpr int BN = TL::BN;
+    constexpr int NKT = TL::NKT;
+    constexpr int ND = TL::ND;
+    constexpr int G = TL::G;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int c32 = lane & 31;
+    const int g = lane >> 5;
+
+    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv);
+    const int b = tc.b, h = tc.h, kvh = h / p.rep;
+    const int S = p.S, W = p.window;
+    const int q0 = tc.qt * kBlockM;
+    const int wrow0 = q0 + wave * 32;
+    const int row = wrow0 + c32;  // this lane's query row
+
+    const T *__restrict__ Q = static_cast<const T *>(p.q);
+    T *__restrict__ O = static_cast<T *>(p.out);
+    const int64_t q_row_stride = (int64_t)p.H * D;
+    const uint32_t kv_stride = (uint32_t)p.Hkv * D * 2;  // bytes between key rows
+    const int64_t kv_head0 = ((int64_t)b * S * p.Hkv + kvh) * D * 2;
+    const uint8_t *Kbh = static_cast<const uint8_t *>(p.k) + kv_head0;
+    const uint8_t *Vbh = static_cast<const uint8_t *>(p.v) + kv_head0;
+
+    // LDS starts zeroed, so a slot no copy writes still holds finite data.
+    for (int i = tid; i < TL::LDS_BYTES / 16; i += kThreads)
+        reinterpret_cast<u32x4 *>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
+
+    // Q fragments: qf[s] = Q[row][16s + 8g .. +7]. Rows past the end of the
+    // sequence read the last row (their results are never stored).
+    u32x4 qf[D / 16];
+    {
+        const T *qrow = Q + ((int64_t)b * S + min(row, S - 1)) * q_row_stride + (int64_t)h * D;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qf[s] = ldg16(qrow + 16 * s + 8 * g) ^ p.q_sign;
+    }
+
+    // Copy offsets: wave w copies key groups w, w+4, w+8, w+12 of K and of V;
+    // lane l fills slot l of the group's 1 KiB block.
+    uint32_t voff_k[4], voff_v[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int kg = wave + 4 * n;
+        const int chunk = lane / G;
+        voff_k[n] = (kg * G + lane % G) * kv_stride + (chunk ^ k_swz<D>(kg)) * 16;
+        voff_v[n] = (kg * G + ((lane % G) ^ v_swz<D>(chunk))) * kv_stride + chunk * 16;
+    }
+    auto copy_tile = [&](int kt, int stage) {
+        const int k0 = kt * BN;
+        // The resource covers rows k0 .. S-1 only; later rows read as zero.
+        const int nrec = (S - 1 - k0) * (int)kv_stride + D * 2;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(Kbh) + (int64_t)k0 * kv_stride, 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(Vbh) + (int64_t)k0 * kv_stride, 0, nrec, kRsrcWord3);
+        uint8_t *kdst = lds + stage * TL::STAGE_BYTES;
+        uint8_t *vdst = kdst + TL::TILE_BYTES;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            lds_copy16(rk, kdst + (wave + 4 * n) * 1024, voff_k[n]);
+            lds_copy16(rv, vdst + (wave + 4 * n) * 1024, voff_v[n]);
+        }
+    };
+
+    // Operand read addresses (bytes within a tile region).
+    // K: lane (c, g) reads K[32t + c][2s + g] at k_addr[t][s % 2] + (s / 2) * 64 G.
+    int k_addr[NKT][2];
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) k_addr[t][par] = k_lds_offset<D>(32 * t + c32, 2 * par + g);
+    // V (transposing reads): lane 16q + j addresses V[4(q/2) + j/4][16(q%2) + 4(j%4)]
+    // plus (16s + 8 half) keys = (16s + 8 half) / G blocks and 32t dims = 64 G t bytes.
+    const int vq = lane >> 4, vj = lane & 15;
+    const int vd = 16 * (vq & 1) + 4 * (vj & 3);
+    const int v_addr = v_lds_offset<D>(4 * (vq >> 1) + (vj >> 2), vd >> 3) + (vd & 7) * 2;
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)(lds);
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int t = 0; t < ND; ++t) oacc[t] = f32x16{};
+    float m_run = -INFINITY;  // running max, in scaled log2 units
+    float l_run = 0.0f;       // this lane's share of the running sum
+    const float sl2e = p.scale_log2;
+
+    int kt_begin, kt_end;
+    key_tile_range<MASK, BN>(q0, S, W, kt_begin, kt_end);
+
+    // One PV k-step: O^T[t] += V^T(16 keys of step s, dims 32t..) P^T(step s).
+    // v_stage is the LDS byte address of this lane's first V read in the
+    // current stage; every other read of the step is an immediate offset.
+    auto pv_step = [&](auto s_tag, uint32_t v_stage, const u32x4 &pb) {
+        constexpr int s = decltype(s_tag)::value;
+        constexpr int blk_lo = (16 * s) / G * 1024, blk_hi = (16 * s + 8) / G * 1024;
+        u32x2 r[2 * ND];
+        static_for<ND>([&](auto t_tag) {
+            constexpr int t = decltype(t_tag)::value;
+            r[2 * t] = lds_read_tr16<blk_lo + t * 64 * G>(v_stage);
+            r[2 * t + 1] = lds_read_tr16<blk_hi + t * 64 * G>(v_stage);
+        });
+        lds_wait(r);
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+            const u32x4 a = {r[2 * t][0], r[2 * t][1], r[2 * t + 1][0], r[2 * t + 1][1]};
+            oacc[t] = mfma16<T>(a, pb, oacc[t]);
+        }
+    };
+
+    __syncthreads();  // LDS zeroed before the first copy lands
+    copy_tile(kt_begin, 0);
+    wait_copies();
+    __syncthreads();
+
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+        const int stage = (kt - kt_begin) & 1;
+        if (kt + 1 < kt_end) copy_tile(kt + 1, stage ^ 1);
+
+        const int k0 = kt * BN;
+        const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
+        // One copy of the tile body per class, so that fully visible tiles
+        // carry no per-element mask test.
+        auto tile_body = [&](auto edge_tag) {
+            constexpr bool EDGE = decltype(edge_tag)::value;
+            const uint8_t *Ks = lds + stage * TL::STAGE_BYTES;
+
+            // S^T = K Q^T.
+            f32x16 sacc[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) sacc[t] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                        Ks + k_addr[t][s & 1] + (s >> 1) * 64 * G);
+                    sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
+                }
+
+            // Mask (edge tiles only) and the running max.
+            if constexpr (EDGE) {
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+                        if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+            mx = half_max(mx);
+            const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2e;
+            if (wave_any(mt > m_run + kRescaleLog2)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < ND; ++t) oacc[t] *= alpha;
+                m_run = m_new;
+            }
+            const float base = (m_run == -INFINITY) ? 0.0f : m_run;
+
+            // P = exp2(s * scale log2e - m), rounded to T; l += sum of the
+            // rounded values; O^T += V^T P^T.
+            const uint32_t v_stage = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES + v_addr;
+            static_for<BN / 16>([&](auto s_tag) {
+                constexpr int s = decltype(s_tag)::value;
+                constexpr int o8 = 8 * (s & 1);
+                float e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float x = sacc[s >> 1][o8 + i];
+                    e[i] = exp2_fast(fmaf(x, sl2e, -base));
+                    if (EDGE && x == -INFINITY) e[i] = 0.0f;
+                }
+                u32x4 pb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pb[i] = pack2<T>(e[2 * i], e[2 * i + 1]);
+                    l_run = sum2<T>(pb[i], l_run);
+                }
+                pv_step(s_tag, v_stage, pb);
+            });
+        };
+        if (cls == kFull) tile_body(std::false_type{});
+        else if (cls == kEdge) tile_body(std::true_type{});
+
+        wait_copies();    // this wave's copies of the next tile have landed
+        __syncthreads();  // ... and everyone's; the current stage is free again
+    }
+
+    // Epilogue: O = O^T / l, written back in BSHD.
+    const float inv = 1.0f / half_sum(l_run);
+    if (row < S) {
+        T *orow = O + ((int64_t)b * S + row) * q_row_stride + (int64_t)h * D;
+#pragma unroll
+        for (int t = 0; t < ND; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 w = {pack2<T>(oacc[t][4 * i] * inv, oacc[t][4 * i + 1] * inv),
+                                 pack2<T>(oacc[t][4 * i + 2] * inv, oacc[t][4 * i + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * i + 4 * g) = w;
+            }
+    }
+}
+
+}  // namespace fa355

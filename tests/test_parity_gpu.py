@@ -219,3 +219,23 @@ def test_rejects_through_binding():
     with pytest.raises(fa.FA355Error) as e:
         fa.attention(*_dev(q, k, v), 0.1, "none")
     assert e.value.status == fa.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64), ("f32", 128)])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_rows_past_the_end_are_never_used(dt, D, mask):
+    """K and V end exactly where NaN-filled memory begins; a ragged last key
+    tile must neither read nor use rows past S (a NaN would reach the output)."""
+    B, S, H, Hkv = 2, 300, 4, 2
+    q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=13)
+    note(f"tail guard {dt} D{D} {mask}")
+
+    def guarded(t):
+        n = t.numel()
+        buf = torch.full((n + 256 * Hkv * D,), float("nan"), dtype=t.dtype, device=DEV)
+        buf[:n] = t.flatten().to(DEV)
+        return buf[:n].view(t.shape)
+
+    out = fa.attention(q.to(DEV), guarded(k), guarded(v), 1.0 / math.sqrt(D), mask)
+    torch.cuda.synchronize()
+    check(out.cpu(), oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask), dt, f"tail {dt} {mask}")
