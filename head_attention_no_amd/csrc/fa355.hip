@@ -145,7 +145,10 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
-    p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+    // A scale below 1e-30 in magnitude is taken as 1e-30: for any fp32 score
+    // |s| < 1e20 the exponent then stays below 1e-10 and exp2 rounds to
+    // exactly 1, as with scale 0, while hidden scores (-inf) still give 0.
+    p.scale_log2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
     const bool neg = std::signbit(scale) && scale != 0.0f;
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
 

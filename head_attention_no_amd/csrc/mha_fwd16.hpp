@@ -104,12 +104,16 @@ __device__ inline u32x2 lds_read_tr16(uint32_t addr)
     return r;
 }
 
-// Wait until every LDS read this wave issued has returned, and make the
-// registers in `r` depend on that wait.
-template <int N>
+// Wait until at most PENDING of this wave's LDS operations are outstanding
+// (LDS operations complete in issue order, so every read issued before the
+// PENDING most recent ones has returned), and make the registers in `r`
+// depend on that wait. PENDING counts only reads issued after those in `r`;
+// anything else issued later only makes the wait stricter.
+template <int PENDING, int N>
 __device__ inline void lds_wait(u32x2 (&r)[N])
 {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_assert(PENDING >= 0 && PENDING <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(PENDING) : "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
 }
@@ -221,25 +225,8 @@ void mha_fwd16(Params p)
     int kt_begin, kt_end;
     key_tile_range<MASK, BN>(q0, S, W, kt_begin, kt_end);
 
-    // One PV k-step: O^T[t] += V^T(16 keys of step s, dims 32t..) P^T(step s).
-    // v_stage is the LDS byte address of this lane's first V read in the
-    // current stage; every other read of the step is an immediate offset.
-    auto pv_step = [&](auto s_tag, uint32_t v_stage, const u32x4 &pb) {
-        constexpr int s = decltype(s_tag)::value;
-        constexpr int blk_lo = (16 * s) / G * 1024, blk_hi = (16 * s + 8) / G * 1024;
-        u32x2 r[2 * ND];
-        static_for<ND>([&](auto t_tag) {
-            constexpr int t = decltype(t_tag)::value;
-            r[2 * t] = lds_read_tr16<blk_lo + t * 64 * G>(v_stage);
-            r[2 * t + 1] = lds_read_tr16<blk_hi + t * 64 * G>(v_stage);
-        });
-        lds_wait(r);
-#pragma unroll
-        for (int t = 0; t < ND; ++t) {
-            const u32x4 a = {r[2 * t][0], r[2 * t][1], r[2 * t + 1][0], r[2 * t + 1][1]};
-            oacc[t] = mfma16<T>(a, pb, oacc[t]);
-        }
-    };
+    constexpr int NPV = BN / 16;  // PV k-steps per tile
+    constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step
 
     __syncthreads();  // LDS zeroed before the first copy lands
     copy_tile(kt_begin, 0);
@@ -252,10 +239,7 @@ void mha_fwd16(Params p)
 
         const int k0 = kt * BN;
         const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
-        // One copy of the tile body per class, so that fully visible tiles
-        // carry no per-element mask test.
-        auto tile_body = [&](auto edge_tag) {
-            constexpr bool EDGE = decltype(edge_tag)::value;
+        if (cls != kEmpty) {
             const uint8_t *Ks = lds + stage * TL::STAGE_BYTES;
 
             // S^T = K Q^T.
@@ -271,8 +255,9 @@ void mha_fwd16(Params p)
                     sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
                 }
 
-            // Mask (edge tiles only) and the running max.
-            if constexpr (EDGE) {
+            // Edge tiles only: hidden scores become -inf, so exp2 gives them
+            // exactly 0 below (the scale is never below 1e-30).
+            if (cls == kEdge) {
 #pragma unroll
                 for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -281,13 +266,33 @@ void mha_fwd16(Params p)
                         if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
                     }
             }
+
+            // V^T operands: the reads for PV k-steps s and s+1 are in flight
+            // while the exponentials of step s are computed.
+            const uint32_t v_stage = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES + v_addr;
+            u32x2 vr[NPV][NVR];
+            auto issue_v = [&](auto s_tag) {
+                constexpr int s = decltype(s_tag)::value;
+                if constexpr (s < NPV) {
+                    constexpr int blk_lo = (16 * s) / G * 1024, blk_hi = (16 * s + 8) / G * 1024;
+                    static_for<ND>([&](auto t_tag) {
+                        constexpr int t = decltype(t_tag)::value;
+                        vr[s][2 * t] = lds_read_tr16<blk_lo + t * 64 * G>(v_stage);
+                        vr[s][2 * t + 1] = lds_read_tr16<blk_hi + t * 64 * G>(v_stage);
+                    });
+                }
+            };
+            issue_v(std::integral_constant<int, 0>{});
+            issue_v(std::integral_constant<int, 1>{});
+
+            // Running max; raised (and O, l rescaled) only when it grows by
+            // more than 2^kRescaleLog2.
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-            mx = half_max(mx);
-            const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2e;
+            const float mt = half_max(mx) * sl2e;
             if (wave_any(mt > m_run + kRescaleLog2)) {
                 const float m_new = fmaxf(m_run, mt);
                 const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - m_new);
@@ -300,28 +305,27 @@ void mha_fwd16(Params p)
 
             // P = exp2(s * scale log2e - m), rounded to T; l += sum of the
             // rounded values; O^T += V^T P^T.
-            const uint32_t v_stage = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES + v_addr;
-            static_for<BN / 16>([&](auto s_tag) {
+            static_for<NPV>([&](auto s_tag) {
                 constexpr int s = decltype(s_tag)::value;
                 constexpr int o8 = 8 * (s & 1);
-                float e[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float x = sacc[s >> 1][o8 + i];
-                    e[i] = exp2_fast(fmaf(x, sl2e, -base));
-                    if (EDGE && x == -INFINITY) e[i] = 0.0f;
-                }
                 u32x4 pb;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pb[i] = pack2<T>(e[2 * i], e[2 * i + 1]);
+                    const float e0 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i], sl2e, -base));
+                    const float e1 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i + 1], sl2e, -base));
+                    pb[i] = pack2<T>(e0, e1);
                     l_run = sum2<T>(pb[i], l_run);
                 }
-                pv_step(s_tag, v_stage, pb);
+                lds_wait<(s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
+#pragma unroll
+                for (int t = 0; t < ND; ++t) {
+                    const u32x4 a = {vr[s][2 * t][0], vr[s][2 * t][1], vr[s][2 * t + 1][0],
+                                     vr[s][2 * t + 1][1]};
+                    oacc[t] = mfma16<T>(a, pb, oacc[t]);
+                }
+                issue_v(std::integral_constant<int, s + 2>{});
             });
-        };
-        if (cls == kFull) tile_body(std::false_type{});
-        else if (cls == kEdge) tile_body(std::true_type{});
+        }
 
         wait_copies();    // this wave's copies of the next tile have landed
         __syncthreads();  // ... and everyone's; the current stage is free again
