@@ -36,7 +36,14 @@ bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
     return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
+#ifndef FA355_WAVES16
+#define FA355_WAVES16 8
+#endif
+// Waves per workgroup of the 16-bit kernel (32 query rows each).
+constexpr int kWaves16 = FA355_WAVES16;
+
 int block_n(int dtype, int D) { return dtype == FA355_F32 ? 32 : 8192 / D; }
+int block_m(int dtype) { return dtype == FA355_F32 ? fa355::kBlockM32 : 32 * kWaves16; }
 
 // Shape checks shared by mha_no_cache and fa355_plan.
 int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
@@ -46,7 +53,7 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     if (dtype != FA355_F32 && dtype != FA355_BF16 && dtype != FA355_F16)
         return FA355_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA355_ERR_UNSUPPORTED;
-    const int64_t n_qtiles = ((int64_t)S + fa355::kBlockM - 1) / fa355::kBlockM;
+    const int64_t n_qtiles = ((int64_t)S + block_m(dtype) - 1) / block_m(dtype);
     if (n_qtiles * B * H > INT32_MAX) return FA355_ERR_UNSUPPORTED;
     // The 16-bit kernel addresses one (batch, K/V head) slice with 32-bit
     // byte offsets: S rows of Hkv * D elements must stay below 2 GiB.
@@ -76,12 +83,13 @@ template <typename T, int D, int MASK>
 hipError_t launch_one(const Params &p, int grid, hipStream_t stream)
 {
     void *args[] = {const_cast<Params *>(&p)};
-    const void *fn;
     if constexpr (std::is_same_v<T, float>)
-        fn = reinterpret_cast<const void *>(&fa355::mha_fwd32<D, MASK>);
+        return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd32<D, MASK>),
+                               dim3(grid), dim3(fa355::kThreads32), args, 0, stream);
     else
-        fn = reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK>);
-    return hipLaunchKernel(fn, dim3(grid), dim3(fa355::kThreads), args, 0, stream);
+        return hipLaunchKernel(
+            reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK, kWaves16>), dim3(grid),
+            dim3(64 * kWaves16), args, 0, stream);
 }
 
 template <typename T, int D>
@@ -141,7 +149,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.H = H;
     p.Hkv = Hkv;
     p.rep = H / Hkv;
-    p.n_qtiles = (S + fa355::kBlockM - 1) / fa355::kBlockM;
+    p.n_qtiles = (S + block_m(dtype) - 1) / block_m(dtype);
     p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
@@ -172,14 +180,14 @@ extern "C" const char *fa355_strerror(int status)
 extern "C" const char *fa355_version(void) { return "fa355 0.1.0 gfx950"; }
 
 extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups,
-                          int *block_m, int *block_n_out, int *tiles, int n)
+                          int *block_m_out, int *block_n_out, int *tiles, int n)
 {
     const int rc = check_shape(B, S, H, Hkv, D, dtype);
     if (rc != FA355_OK) return rc;
-    const int n_qtiles = (S + fa355::kBlockM - 1) / fa355::kBlockM;
+    const int n_qtiles = (S + block_m(dtype) - 1) / block_m(dtype);
     const int grid = n_qtiles * B * H;
     if (num_workgroups) *num_workgroups = grid;
-    if (block_m) *block_m = fa355::kBlockM;
+    if (block_m_out) *block_m_out = block_m(dtype);
     if (block_n_out) *block_n_out = block_n(dtype, D);
     if (tiles) {
         if (n < 0) return FA355_ERR_INVALID_ARG;

@@ -35,14 +35,11 @@ struct Params {
     const void *v;
     int B, S, H, Hkv;
     int rep;       // H / Hkv: query heads per K/V head
-    int n_qtiles;  // ceil(S / kBlockM)
+    int n_qtiles;  // ceil(S / query rows per workgroup)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|
 };
-
-constexpr int kThreads = 256;  // 4 waves of 64 lanes
-constexpr int kBlockM = 128;   // query rows per workgroup (32 per wave)
 
 // Lazy rescaling: the running max is only raised when a new tile's max
 // exceeds it by more than this many powers of two, so P stays <= 2^8 and
@@ -110,11 +107,11 @@ __device__ inline bool visible(int row, int key, int S, int W)
     return true;
 }
 
-// Key-tile range [begin, end) a workgroup whose first row is q0 must visit.
-template <int MASK, int BN>
+// Key-tile range [begin, end) a workgroup of BM rows starting at q0 must visit.
+template <int MASK, int BM, int BN>
 __device__ inline void key_tile_range(int q0, int S, int W, int &begin, int &end)
 {
-    const int q_last = min(q0 + kBlockM, S) - 1;
+    const int q_last = min(q0 + BM, S) - 1;
     begin = 0;
     end = (S + BN - 1) / BN;
     if (MASK != kMaskNone) end = min(end, q_last / BN + 1);

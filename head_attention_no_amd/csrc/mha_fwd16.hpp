@@ -67,7 +67,7 @@ struct Tile16 {
     static constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered
     static constexpr int GROUPS = BN / G;         // key groups per tile
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(GROUPS == 16, "4 waves x 4 key groups of K and of V per tile");
+    static_assert(GROUPS == 16, "16 key groups of K and of V per tile");
 };
 
 template <int D>
@@ -127,11 +127,15 @@ __device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds_dst,
 // Wait for this wave's outstanding global -> LDS copies (vmcnt = 0).
 __device__ inline void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename T, int D, int MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup (4 or 8), 32 query rows each.
+template <typename T, int D, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_fwd16(Params p)
 {
     using TL = Tile16<D>;
+    constexpr int NTHREADS = 64 * NW;
+    constexpr int BM = 32 * NW;
+    constexpr int NCOPY = 16 / NW;  // key groups of K (and of V) each wave copies per tile
     constexpr int BN = TL::BN;
     constexpr int NKT = TL::NKT;
     constexpr int ND = TL::ND;
@@ -148,7 +152,7 @@ void mha_fwd16(Params p)
     const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv);
     const int b = tc.b, h = tc.h, kvh = h / p.rep;
     const int S = p.S, W = p.window;
-    const int q0 = tc.qt * kBlockM;
+    const int q0 = tc.qt * BM;
     const int wrow0 = q0 + wave * 32;
     const int row = wrow0 + c32;  // this lane's query row
 
@@ -161,7 +165,7 @@ void mha_fwd16(Params p)
     const uint8_t *Vbh = static_cast<const uint8_t *>(p.v) + kv_head0;
 
     // LDS starts zeroed, so a slot no copy writes still holds finite data.
-    for (int i = tid; i < TL::LDS_BYTES / 16; i += kThreads)
+    for (int i = tid; i < TL::LDS_BYTES / 16; i += NTHREADS)
         reinterpret_cast<u32x4 *>(lds)[i] = u32x4{0u, 0u, 0u, 0u};
 
     // Q fragments: qf[s] = Q[row][16s + 8g .. +7]. Rows past the end of the
@@ -173,32 +177,34 @@ void mha_fwd16(Params p)
         for (int s = 0; s < D / 16; ++s) qf[s] = ldg16(qrow + 16 * s + 8 * g) ^ p.q_sign;
     }
 
-    // Copy offsets: wave w copies key groups w, w+4, w+8, w+12 of K and of V;
+    // Copy offsets: wave w copies key groups w, w+NW, ... of K and of V;
     // lane l fills slot l of the group's 1 KiB block.
-    uint32_t voff_k[4], voff_v[4];
+    uint32_t voff_k[NCOPY], voff_v[NCOPY];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int kg = wave + 4 * n;
+    for (int n = 0; n < NCOPY; ++n) {
+        const int kg = wave + NW * n;
         const int chunk = lane / G;
         voff_k[n] = (kg * G + lane % G) * kv_stride + (chunk ^ k_swz<D>(kg)) * 16;
         voff_v[n] = (kg * G + ((lane % G) ^ v_swz<D>(chunk))) * kv_stride + chunk * 16;
     }
-    auto copy_tile = [&](int kt, int stage) {
+    auto tile_rsrc = [&](const uint8_t *base, int kt) {
         const int k0 = kt * BN;
         // The resource covers rows k0 .. S-1 only; later rows read as zero.
         const int nrec = (S - 1 - k0) * (int)kv_stride + D * 2;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(Kbh) + (int64_t)k0 * kv_stride, 0, nrec, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t *>(Vbh) + (int64_t)k0 * kv_stride, 0, nrec, kRsrcWord3);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base) + (int64_t)k0 * kv_stride,
+                                                 0, nrec, kRsrcWord3);
+    };
+    auto copy_tile = [&](int kt, int stage) {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(Kbh, kt), rv = tile_rsrc(Vbh, kt);
         uint8_t *kdst = lds + stage * TL::STAGE_BYTES;
         uint8_t *vdst = kdst + TL::TILE_BYTES;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            lds_copy16(rk, kdst + (wave + 4 * n) * 1024, voff_k[n]);
-            lds_copy16(rv, vdst + (wave + 4 * n) * 1024, voff_v[n]);
+        for (int n = 0; n < NCOPY; ++n) {
+            lds_copy16(rk, kdst + (wave + NW * n) * 1024, voff_k[n]);
+            lds_copy16(rv, vdst + (wave + NW * n) * 1024, voff_v[n]);
         }
     };
+    auto land_tile = [&](int) { wait_copies(); };
 
     // Operand read addresses (bytes within a tile region).
     // K: lane (c, g) reads K[32t + c][2s + g] at k_addr[t][s % 2] + (s / 2) * 64 G.
@@ -223,14 +229,14 @@ void mha_fwd16(Params p)
     const float sl2e = p.scale_log2;
 
     int kt_begin, kt_end;
-    key_tile_range<MASK, BN>(q0, S, W, kt_begin, kt_end);
+    key_tile_range<MASK, BM, BN>(q0, S, W, kt_begin, kt_end);
 
     constexpr int NPV = BN / 16;  // PV k-steps per tile
     constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step
 
     __syncthreads();  // LDS zeroed before the first copy lands
     copy_tile(kt_begin, 0);
-    wait_copies();
+    land_tile(0);
     __syncthreads();
 
     for (int kt = kt_begin; kt < kt_end; ++kt) {
@@ -327,7 +333,7 @@ void mha_fwd16(Params p)
             });
         }
 
-        wait_copies();    // this wave's copies of the next tile have landed
+        if (kt + 1 < kt_end) land_tile(stage ^ 1);  // this wave's part of the next tile
         __syncthreads();  // ... and everyone's; the current stage is free again
     }
 

@@ -20,6 +20,9 @@
 
 namespace fa355 {
 
+constexpr int kThreads32 = 256;  // 4 waves of 64 lanes
+constexpr int kBlockM32 = 128;   // query rows per workgroup (32 per wave)
+
 template <int D>
 struct Tile32 {
     static constexpr int BN = 32;       // keys per tile
@@ -32,7 +35,7 @@ struct Tile32 {
 };
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_fwd32(Params p)
 {
     using TL = Tile32<D>;
@@ -50,7 +53,7 @@ void mha_fwd32(Params p)
     const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv);
     const int b = tc.b, h = tc.h, kvh = h / p.rep;
     const int S = p.S, W = p.window;
-    const int q0 = tc.qt * kBlockM;
+    const int q0 = tc.qt * kBlockM32;
     const int wrow0 = q0 + wave * 32;
     const int row = wrow0 + c32;  // this lane's query row
 
@@ -78,11 +81,11 @@ void mha_fwd32(Params p)
     }
 
     int kt_begin, kt_end;
-    key_tile_range<MASK, BN>(q0, S, W, kt_begin, kt_end);
+    key_tile_range<MASK, kBlockM32, BN>(q0, S, W, kt_begin, kt_end);
 
     // Staging: every thread moves D/32 rows x 16 bytes of K and of V.
     constexpr int CPR = D / 4;
-    constexpr int STEP = kThreads / CPR;
+    constexpr int STEP = kThreads32 / CPR;
     constexpr int R = BN / STEP;
     u32x4 stg[2 * R];
     auto load_tile = [&](int kt) {

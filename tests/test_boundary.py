@@ -82,7 +82,7 @@ def test_plan_covers_every_tile_once(shape):
     B, S, H, Hkv, D, dt = shape
     pl = fa.plan(B, S, H, Hkv, D, dt, with_tiles=True)
     nq = -(-S // pl["block_m"])
-    assert pl["block_m"] == 128
+    assert pl["block_m"] == (128 if dt == fa.F32 else 256)
     assert pl["block_n"] == (32 if dt == fa.F32 else 8192 // D)
     assert pl["num_workgroups"] == nq * B * H
     tiles = pl["tiles"]
