@@ -138,13 +138,40 @@ def copy_calibration(mib: int, steps: int, warmup: int):
             "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}
 
 
+def kernel_sources_hash() -> str:
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "head_attention_no_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter
+    runs (profiles/*.traffic.json), scaled by a plain copy's counters; None
+    when no file covers this workload or the kernel sources changed since."""
+    import glob
+
+    cur = kernel_sources_hash()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
+        with open(f) as fh:
+            d = json.load(fh)
+        if d.get("workload") == w.name and d.get("kernel_sources_sha256_16") == cur:
+            return int(d["traffic_bytes_per_launch"]), os.path.basename(f)
+    return None, None
+
+
 def roofline(w, t):
     fl = flops(w)
     achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    traffic, src = measured_traffic(w)
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": KERNEL_NAME, "flop_per_launch": fl,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
+            "traffic_source": src, "kernel": KERNEL_NAME, "flop_per_launch": fl,
             "launch_ms_mean": round(t["launch_ms_mean"], 5)}
 
 
