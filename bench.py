@@ -241,7 +241,7 @@ def main():
     line = one_line(w, args, t, cpu)
     if args.all:
         others = {}
-        for o in inputs.WORKLOADS:
+        for o in inputs.WORKLOADS + inputs.WIDER:
             if o.name == w.name:
                 continue
             print(f"# timing {o.name}", file=sys.stderr, flush=True)

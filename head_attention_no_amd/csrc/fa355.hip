@@ -23,7 +23,7 @@ const char *const kStatusText[] = {
     "success",
     "invalid argument (null pointer, size < 1, H not a multiple of Hkv, unknown dtype or mask, "
     "window < 1 with the sliding mask, non-finite scale, or out overlapping an input)",
-    "unsupported (head dim other than 64 or 128, pointer not 16-byte aligned, grid too large, or one K/V head slice of 2 GiB or more)",
+    "unsupported (head dim other than 32, 64, 128 or 256, pointer not 16-byte aligned, grid too large, or one K/V head slice of 2 GiB or more)",
     "no usable device (no current HIP device, or it is not gfx950)",
     "kernel launch failed",
 };
@@ -36,14 +36,31 @@ bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
     return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
-#ifndef FA355_WAVES16
-#define FA355_WAVES16 8
-#endif
-// Waves per workgroup of the 16-bit kernel (32 query rows each).
-constexpr int kWaves16 = FA355_WAVES16;
+bool supported_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
-int block_n(int dtype, int D) { return dtype == FA355_F32 ? 32 : 8192 / D; }
-int block_m(int dtype) { return dtype == FA355_F32 ? fa355::kBlockM32 : 32 * kWaves16; }
+// Tile shape of the kernel instance for (dtype, D); D must be supported.
+template <int D>
+int block_m16() { return 32 * fa355::Tile16<D>::NW; }
+int block_m(int dtype, int D)
+{
+    if (dtype == FA355_F32) return fa355::kBlockM32;
+    switch (D) {
+    case 32: return block_m16<32>();
+    case 64: return block_m16<64>();
+    case 128: return block_m16<128>();
+    default: return block_m16<256>();
+    }
+}
+int block_n(int dtype, int D)
+{
+    if (dtype == FA355_F32) return fa355::Tile32<64>::BN;
+    switch (D) {
+    case 32: return fa355::Tile16<32>::BN;
+    case 64: return fa355::Tile16<64>::BN;
+    case 128: return fa355::Tile16<128>::BN;
+    default: return fa355::Tile16<256>::BN;
+    }
+}
 
 // Shape checks shared by mha_no_cache and fa355_plan.
 int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
@@ -52,8 +69,8 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     if (H % Hkv != 0) return FA355_ERR_INVALID_ARG;
     if (dtype != FA355_F32 && dtype != FA355_BF16 && dtype != FA355_F16)
         return FA355_ERR_INVALID_ARG;
-    if (D != 64 && D != 128) return FA355_ERR_UNSUPPORTED;
-    const int64_t n_qtiles = ((int64_t)S + block_m(dtype) - 1) / block_m(dtype);
+    if (!supported_dim(D)) return FA355_ERR_UNSUPPORTED;
+    const int64_t n_qtiles = ((int64_t)S + block_m(dtype, D) - 1) / block_m(dtype, D);
     if (n_qtiles * B * H > INT32_MAX) return FA355_ERR_UNSUPPORTED;
     // The 16-bit kernel addresses one (batch, K/V head) slice with 32-bit
     // byte offsets: S rows of Hkv * D elements must stay below 2 GiB.
@@ -87,9 +104,8 @@ hipError_t launch_one(const Params &p, int grid, hipStream_t stream)
         return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd32<D, MASK>),
                                dim3(grid), dim3(fa355::kThreads32), args, 0, stream);
     else
-        return hipLaunchKernel(
-            reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK, kWaves16>), dim3(grid),
-            dim3(64 * kWaves16), args, 0, stream);
+        return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK>),
+                               dim3(grid), dim3(64 * fa355::Tile16<D>::NW), args, 0, stream);
 }
 
 template <typename T, int D>
@@ -105,8 +121,12 @@ hipError_t launch_mask(const Params &p, int mask, int grid, hipStream_t stream)
 template <typename T>
 hipError_t launch_dim(const Params &p, int D, int mask, int grid, hipStream_t stream)
 {
-    return D == 64 ? launch_mask<T, 64>(p, mask, grid, stream)
-                   : launch_mask<T, 128>(p, mask, grid, stream);
+    switch (D) {
+    case 32: return launch_mask<T, 32>(p, mask, grid, stream);
+    case 64: return launch_mask<T, 64>(p, mask, grid, stream);
+    case 128: return launch_mask<T, 128>(p, mask, grid, stream);
+    default: return launch_mask<T, 256>(p, mask, grid, stream);
+    }
 }
 
 }  // namespace
@@ -149,7 +169,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.H = H;
     p.Hkv = Hkv;
     p.rep = H / Hkv;
-    p.n_qtiles = (S + block_m(dtype) - 1) / block_m(dtype);
+    p.n_qtiles = (S + block_m(dtype, D) - 1) / block_m(dtype, D);
     p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
@@ -184,10 +204,10 @@ extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *n
 {
     const int rc = check_shape(B, S, H, Hkv, D, dtype);
     if (rc != FA355_OK) return rc;
-    const int n_qtiles = (S + block_m(dtype) - 1) / block_m(dtype);
+    const int n_qtiles = (S + block_m(dtype, D) - 1) / block_m(dtype, D);
     const int grid = n_qtiles * B * H;
     if (num_workgroups) *num_workgroups = grid;
-    if (block_m_out) *block_m_out = block_m(dtype);
+    if (block_m_out) *block_m_out = block_m(dtype, D);
     if (block_n_out) *block_n_out = block_n(dtype, D);
     if (tiles) {
         if (n < 0) return FA355_ERR_INVALID_ARG;

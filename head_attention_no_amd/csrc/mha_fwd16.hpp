@@ -56,24 +56,43 @@ namespace fa355 {
 // Word 3 of a raw buffer resource (untyped 32-bit access, range checked).
 constexpr int kRsrcWord3 = 0x00020000;
 
+// Per head dim D: keys per tile BN (S^T tiles and two V steps in flight fit
+// the registers), waves per workgroup NW and waves per SIMD WPE (at D = 256
+// the Q fragments and O^T alone take 192 registers, so one wave per SIMD
+// with the 512-register budget), and the LDS swizzle periods (below).
 template <int D>
 struct Tile16 {
-    static constexpr int BN = 8192 / D;           // keys per tile (64 or 128)
+    static constexpr int BN = D == 32 ? 128 : 8192 / D;  // keys per tile: 128, 128, 64, 32
+    static constexpr int NW = D == 256 ? 4 : 8;           // waves per workgroup, 32 query rows each
+    static constexpr int WPE = D == 256 ? 1 : 2;          // waves per SIMD
     static constexpr int NKT = BN / 32;           // 32-key sub-tiles of S^T
     static constexpr int ND = D / 32;             // 32-dim sub-tiles of O^T
     static constexpr int G = 512 / D;             // keys per 1 KiB key group
-    static constexpr int TILE_BYTES = BN * D * 2;  // 16 KiB
+    static constexpr int TILE_BYTES = BN * D * 2;  // 8 or 16 KiB
     static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile, then V tile
     static constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered
     static constexpr int GROUPS = BN / G;         // key groups per tile
-    static_assert(D == 64 || D == 128, "head dim");
-    static_assert(GROUPS == 16, "16 key groups of K and of V per tile");
+    static constexpr int KP = D == 256 ? 4 : D == 128 ? 2 : 1;  // K read address bases
+    static constexpr int VT = D == 256 ? 2 : 1;   // V read bases per 32-dim sub-tile period
+    static constexpr int VH = D == 32 ? 2 : 1;    // V read bases per 8-key half period
+    static constexpr int V_AHEAD = 2 * ND <= 8 ? 2 : 1;  // PV k-steps whose V reads are in flight
+    static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
+    static_assert(GROUPS % NW == 0, "every wave copies the same number of key groups");
 };
 
+// XOR swizzles of the 1 KiB key-group blocks (kg = key / G, ks = key % G,
+// c = 16-byte chunk of the row): K slot (c ^ k_swz(kg)) G + ks, V slot
+// (c ^ vc_swz(kg)) G + (ks ^ vk_swz(c)). They make the 16 lanes of a K read
+// cycle, and the 32 lanes of a V read cycle, hit 64 distinct banks.
 template <int D>
-__device__ inline int k_swz(int kg) { return kg & (D == 128 ? 3 : 1); }
+__device__ inline int k_swz(int kg) { return kg & (D / 32 - 1); }
 template <int D>
-__device__ inline int v_swz(int chunk) { return D == 128 ? 0 : 4 * ((chunk >> 1) & 1); }
+__device__ inline int vc_swz(int kg) { return D == 256 ? 4 * (kg & 1) : 0; }
+template <int D>
+__device__ inline int vk_swz(int c)
+{
+    return D == 32 ? (4 * ((c >> 1) & 1)) ^ (8 * (c & 1)) : D == 64 ? 4 * ((c >> 1) & 1) : 0;
+}
 
 // Byte offsets of K[key][16-byte chunk c] and V[key][c] inside a tile region.
 template <int D>
@@ -87,7 +106,8 @@ template <int D>
 __device__ inline int v_lds_offset(int key, int c)
 {
     constexpr int G = Tile16<D>::G;
-    return (key / G) * 1024 + (c * G + ((key % G) ^ v_swz<D>(c))) * 16;
+    const int kg = key / G;
+    return kg * 1024 + ((c ^ vc_swz<D>(kg)) * G + ((key % G) ^ vk_swz<D>(c))) * 16;
 }
 
 // Transposing LDS read at byte address addr + OFF (see the layout note above).
@@ -127,15 +147,18 @@ __device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds_dst,
 // Wait for this wave's outstanding global -> LDS copies (vmcnt = 0).
 __device__ inline void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// NW waves per workgroup (4 or 8), 32 query rows each.
-template <typename T, int D, int MASK, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Tile16<D>::NW waves per workgroup, 32 query rows each.
+template <typename T, int D, int MASK>
+__global__ __launch_bounds__(64 * Tile16<D>::NW)
+__attribute__((amdgpu_waves_per_eu(Tile16<D>::WPE, Tile16<D>::WPE)))
 void mha_fwd16(Params p)
 {
     using TL = Tile16<D>;
+    constexpr int NW = TL::NW;
     constexpr int NTHREADS = 64 * NW;
     constexpr int BM = 32 * NW;
-    constexpr int NCOPY = 16 / NW;  // key groups of K (and of V) each wave copies per tile
+    constexpr int NCOPY = TL::GROUPS / NW;  // key groups of K (and of V) each wave copies per tile
+    constexpr int KP = TL::KP, VT = TL::VT, VH = TL::VH, V_AHEAD = TL::V_AHEAD;
     constexpr int BN = TL::BN;
     constexpr int NKT = TL::NKT;
     constexpr int ND = TL::ND;
@@ -183,9 +206,10 @@ void mha_fwd16(Params p)
 #pragma unroll
     for (int n = 0; n < NCOPY; ++n) {
         const int kg = wave + NW * n;
-        const int chunk = lane / G;
-        voff_k[n] = (kg * G + lane % G) * kv_stride + (chunk ^ k_swz<D>(kg)) * 16;
-        voff_v[n] = (kg * G + ((lane % G) ^ v_swz<D>(chunk))) * kv_stride + chunk * 16;
+        const int slot_c = lane / G, slot_k = lane % G;  // lane l fills slot l = slot_c G + slot_k
+        voff_k[n] = (kg * G + slot_k) * kv_stride + (slot_c ^ k_swz<D>(kg)) * 16;
+        const int vc = slot_c ^ vc_swz<D>(kg);
+        voff_v[n] = (kg * G + (slot_k ^ vk_swz<D>(vc))) * kv_stride + vc * 16;
     }
     auto tile_rsrc = [&](const uint8_t *base, int kt) {
         const int k0 = kt * BN;
@@ -207,17 +231,24 @@ void mha_fwd16(Params p)
     auto land_tile = [&](int) { wait_copies(); };
 
     // Operand read addresses (bytes within a tile region).
-    // K: lane (c, g) reads K[32t + c][2s + g] at k_addr[t][s % 2] + (s / 2) * 64 G.
-    int k_addr[NKT][2];
+    // K: lane (c, g) reads K[32t + c][2s + g] at k_addr[t][s % KP] + (s / KP) 2 KP G 16.
+    int k_addr[NKT][KP];
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int par = 0; par < 2; ++par) k_addr[t][par] = k_lds_offset<D>(32 * t + c32, 2 * par + g);
+        for (int p = 0; p < KP; ++p) k_addr[t][p] = k_lds_offset<D>(32 * t + c32, 2 * p + g);
     // V (transposing reads): lane 16q + j addresses V[4(q/2) + j/4][16(q%2) + 4(j%4)]
-    // plus (16s + 8 half) keys = (16s + 8 half) / G blocks and 32t dims = 64 G t bytes.
+    // plus 16s + 8 half keys and 32t dims: base v_addr[t % VT][half % VH] plus
+    // the immediate (16s + 8 (half - half % VH)) / G blocks + (t - t % VT) 64 G bytes.
     const int vq = lane >> 4, vj = lane & 15;
-    const int vd = 16 * (vq & 1) + 4 * (vj & 3);
-    const int v_addr = v_lds_offset<D>(4 * (vq >> 1) + (vj >> 2), vd >> 3) + (vd & 7) * 2;
+    int v_addr[VT][VH];
+#pragma unroll
+    for (int tb = 0; tb < VT; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < VH; ++hb) {
+            const int vd = 32 * tb + 16 * (vq & 1) + 4 * (vj & 3);
+            v_addr[tb][hb] = v_lds_offset<D>(4 * (vq >> 1) + (vj >> 2) + 8 * hb, vd >> 3) + (vd & 7) * 2;
+        }
     const uint32_t lds_base =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)(lds);
 
@@ -257,7 +288,7 @@ void mha_fwd16(Params p)
 #pragma unroll
                 for (int t = 0; t < NKT; ++t) {
                     const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        Ks + k_addr[t][s & 1] + (s >> 1) * 64 * G);
+                        Ks + k_addr[t][s % KP] + (s / KP) * 2 * KP * G * 16);
                     sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
                 }
 
@@ -273,23 +304,29 @@ void mha_fwd16(Params p)
                     }
             }
 
-            // V^T operands: the reads for PV k-steps s and s+1 are in flight
-            // while the exponentials of step s are computed.
-            const uint32_t v_stage = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES + v_addr;
+            // V^T operands: the reads for PV k-steps s .. s+V_AHEAD-1 are in
+            // flight while the exponentials of step s are computed.
+            const uint32_t v_region = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES;
+            uint32_t v_stage[VT][VH];
+#pragma unroll
+            for (int tb = 0; tb < VT; ++tb)
+#pragma unroll
+                for (int hb = 0; hb < VH; ++hb) v_stage[tb][hb] = v_region + v_addr[tb][hb];
             u32x2 vr[NPV][NVR];
             auto issue_v = [&](auto s_tag) {
                 constexpr int s = decltype(s_tag)::value;
                 if constexpr (s < NPV) {
-                    constexpr int blk_lo = (16 * s) / G * 1024, blk_hi = (16 * s + 8) / G * 1024;
                     static_for<ND>([&](auto t_tag) {
                         constexpr int t = decltype(t_tag)::value;
-                        vr[s][2 * t] = lds_read_tr16<blk_lo + t * 64 * G>(v_stage);
-                        vr[s][2 * t + 1] = lds_read_tr16<blk_hi + t * 64 * G>(v_stage);
+                        constexpr int toff = (t - t % VT) * 64 * G;
+                        constexpr int lo = (16 * s) / G * 1024 + toff;
+                        constexpr int hi = (16 * s + 8 * (1 - 1 % VH)) / G * 1024 + toff;
+                        vr[s][2 * t] = lds_read_tr16<lo>(v_stage[t % VT][0]);
+                        vr[s][2 * t + 1] = lds_read_tr16<hi>(v_stage[t % VT][1 % VH]);
                     });
                 }
             };
-            issue_v(std::integral_constant<int, 0>{});
-            issue_v(std::integral_constant<int, 1>{});
+            static_for<V_AHEAD>(issue_v);
 
             // Running max; raised (and O, l rescaled) only when it grows by
             // more than 2^kRescaleLog2.
@@ -322,14 +359,14 @@ void mha_fwd16(Params p)
                     pb[i] = pack2<T>(e0, e1);
                     l_run = sum2<T>(pb[i], l_run);
                 }
-                lds_wait<(s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
+                lds_wait<(V_AHEAD > 1 && s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
 #pragma unroll
                 for (int t = 0; t < ND; ++t) {
                     const u32x4 a = {vr[s][2 * t][0], vr[s][2 * t][1], vr[s][2 * t + 1][0],
                                      vr[s][2 * t + 1][1]};
                     oacc[t] = mfma16<T>(a, pb, oacc[t]);
                 }
-                issue_v(std::integral_constant<int, s + 2>{});
+                issue_v(std::integral_constant<int, s + V_AHEAD>{});
             });
         }
 

@@ -6,8 +6,9 @@
 // owns 32 query rows; key tiles of 32 keys.
 //  * S^T = K Q^T: for k-step s (0 .. D/2-1) lane (c, g) supplies
 //    Q[row c][dsel(s, g)] and K[key c][dsel(s, g)], dsel(s, g) =
-//    s%32 + 64(s/32) + 32g (any split of d between the two lane halves
-//    works; this one keeps each half's Q values contiguous in memory).
+//    s%H + 2H(s/H) + Hg with H = min(32, D/2) (any split of d between the
+//    two lane halves works; this one keeps each half's Q values contiguous
+//    in runs of H).
 //  * The accumulator element 4i+j of lane (c, g) is key 8i + 4g + j of
 //    query c, which is directly the B operand (one key per k-step) of
 //    O^T = V^T P^T; V is read from LDS one fp32 per lane per k-step.
@@ -27,15 +28,18 @@ template <int D>
 struct Tile32 {
     static constexpr int BN = 32;       // keys per tile
     static constexpr int ND = D / 32;   // 32-dim sub-tiles of O^T
+    static constexpr int H = D < 64 ? D / 2 : 32;  // dsel run length
     static constexpr int K_LD = D + 1;  // LDS row strides (floats)
     static constexpr int V_LD = D + 8;
     static constexpr int K_ELEMS = BN * K_LD;
     static constexpr int STAGE = K_ELEMS + BN * V_LD;
-    static_assert(D == 64 || D == 128, "head dim");
+    // At D = 256 the Q fragments and O^T take 256 registers: one wave per SIMD.
+    static constexpr int WPE = D == 256 ? 1 : 2;
+    static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
 };
 
 template <int D, int MASK>
-__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(Tile32<D>::WPE, Tile32<D>::WPE)))
 void mha_fwd32(Params p)
 {
     using TL = Tile32<D>;
@@ -75,7 +79,7 @@ void mha_fwd32(Params p)
         const float *qrow = Q + ((int64_t)b * S + min(row, S - 1)) * q_row_stride + (int64_t)h * D;
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-            const int d = (4 * s) % 32 + 64 * ((4 * s) / 32) + 32 * g;
+            const int d = (4 * s) % TL::H + 2 * TL::H * ((4 * s) / TL::H) + TL::H * g;
             qf[s] = ldg16(qrow + d) ^ p.q_sign;
         }
     }
@@ -138,7 +142,7 @@ void mha_fwd32(Params p)
             f32x16 sacc = f32x16{};
 #pragma unroll
             for (int s = 0; s < D / 2; ++s) {
-                const int d = (s % 32) + 64 * (s / 32) + 32 * g;
+                const int d = s % TL::H + 2 * TL::H * (s / TL::H) + TL::H * g;
                 const float a = Kf[c32 * TL::K_LD + d];
                 const float bq = __uint_as_float(qf[s / 4][s % 4]);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bq, sacc, 0, 0, 0);

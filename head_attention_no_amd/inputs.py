@@ -12,7 +12,8 @@ that any run reproduces the same bits:
 
 The named workloads are the five shapes this library is measured and
 checked on: long-context causal and sliding-window attention with grouped
-K/V heads, plus a small fp32 case and a peaked-softmax fp16 case.
+K/V heads, plus a small fp32 case and a peaked-softmax fp16 case; WIDER adds
+the head dims 32 and 256.
 """
 from __future__ import annotations
 
@@ -61,7 +62,14 @@ WORKLOADS = [
              k_mult=4.0, seed=1005),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Head dims 32 and 256 (the rest of the op's shape contract), sized to the
+# same causal FLOP count as the S = 4096 grouped workload above.
+WIDER = [
+    Workload("mha_b4_s8192_h16_d32_bf16_causal", 4, 8192, 16, 16, 32, "bf16", "causal", seed=1006),
+    Workload("mha_b2_s4096_h16_d256_bf16_causal", 2, 4096, 16, 16, 256, "bf16", "causal", seed=1007),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS + WIDER}
 
 
 def make_qkv(B: int, S: int, H: int, Hkv: int, D: int, dtype: str = "bf16", seed: int = 0,

@@ -81,8 +81,8 @@ typedef enum {
  *   stream               a hipStream_t, or NULL for the null stream; stands
  *                        in for the page's DeviceContext.
  *
- * Supported today: D in {64, 128}; any S >= 1 (ragged tails are masked);
- * all three dtypes. Pointers must be 16-byte aligned; out must not overlap
+ * Supported today: D in {32, 64, 128, 256}; any S >= 1 (ragged tails are
+ * masked); all three dtypes. Pointers must be 16-byte aligned; out must not overlap
  * q, k or v. Element offsets are computed in 64 bits.
  *
  * Ownership: the caller owns every buffer; the library reads q, k, v and

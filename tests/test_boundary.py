@@ -60,7 +60,7 @@ def test_invalid_arguments(over):
 
 
 @pytest.mark.parametrize("over", [
-    dict(D=32), dict(D=96), dict(D=256),
+    dict(D=16), dict(D=96), dict(D=512),
     dict(q=P2 + 2), dict(out=P1 + 8), dict(k=P3 + 4), dict(v=P4 + 1),
     dict(B=1 << 12, S=1 << 17, H=1 << 10, Hkv=1 << 10, out=1 << 47, q=2 << 47, k=3 << 47,
          v=4 << 47),                  # 2^32 workgroups
@@ -77,13 +77,16 @@ def test_unsupported_arguments(over):
     (1, 128, 4, 4, 64, fa.F32),       # 4 groups: fallback order
     (3, 300, 6, 2, 64, fa.BF16),      # ragged S, 6 groups
     (1, 1, 1, 1, 128, fa.F16),
+    (2, 1000, 8, 2, 32, fa.BF16),
+    (1, 777, 8, 8, 256, fa.F16),      # 128-row tiles at D = 256
+    (1, 300, 4, 2, 256, fa.F32),
 ])
 def test_plan_covers_every_tile_once(shape):
     B, S, H, Hkv, D, dt = shape
     pl = fa.plan(B, S, H, Hkv, D, dt, with_tiles=True)
     nq = -(-S // pl["block_m"])
-    assert pl["block_m"] == (128 if dt == fa.F32 else 256)
-    assert pl["block_n"] == (32 if dt == fa.F32 else 8192 // D)
+    assert pl["block_m"] == (128 if dt == fa.F32 or D == 256 else 256)
+    assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 128, 128: 64, 256: 32}[D])
     assert pl["num_workgroups"] == nq * B * H
     tiles = pl["tiles"]
     assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B) for h in range(H))
@@ -110,8 +113,9 @@ def test_plan_keeps_shared_kv_heads_on_one_xcd():
 def test_plan_rejects_like_the_entry_point():
     with pytest.raises(fa.FA355Error):
         fa.plan(1, 128, 4, 3, 64, fa.BF16)
-    with pytest.raises(fa.FA355Error):
-        fa.plan(1, 128, 4, 4, 48, fa.BF16)
+    for D in (16, 48, 96, 512):
+        with pytest.raises(fa.FA355Error):
+            fa.plan(1, 128, 4, 4, D, fa.BF16)
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -1,6 +1,7 @@
 """Host model of the 16-bit kernel's LDS layouts (CPU only).
 
-Restates the slot formulas of mha_fwd16.hpp and checks, for D = 64 and 128:
+Restates the slot formulas of mha_fwd16.hpp and checks, for D = 32, 64,
+128 and 256:
   - the global -> LDS copy maps (lane l of a copy fills 16-byte slot l of a
     1 KiB key-group block) cover every (key, 16-byte chunk) of a tile once;
   - every operand read of a tile is one per-lane base plus an immediate;
@@ -15,16 +16,28 @@ The GPU parity tests check the kernel itself; this pins the layout algebra.
 import pytest
 
 
+DIMS = [32, 64, 128, 256]
+TILE_KEYS = {32: 128, 64: 128, 128: 64, 256: 32}
+K_BASES = {32: 1, 64: 1, 128: 2, 256: 4}      # k-step period of the K read bases
+V_BASES = {32: (1, 2), 64: (1, 1), 128: (1, 1), 256: (2, 1)}  # (sub-tile, half) periods
+
+
 def cfg(D):
-    return 512 // D, D // 8, 8192 // D  # keys per 1 KiB group, chunks per row, keys per tile
+    return 512 // D, D // 8, TILE_KEYS[D]  # keys per 1 KiB group, chunks per row, keys per tile
 
 
 def swK(D, kg):
-    return kg & (3 if D == 128 else 1)
+    return kg & (D // 32 - 1)
 
 
-def swV(D, c):
-    return 0 if D == 128 else 4 * ((c >> 1) & 1)
+def swVc(D, kg):
+    return 4 * (kg & 1) if D == 256 else 0
+
+
+def swVk(D, c):
+    if D == 32:
+        return (4 * ((c >> 1) & 1)) ^ (8 * (c & 1))
+    return 4 * ((c >> 1) & 1) if D == 64 else 0
 
 
 def k_byte(D, key, c):
@@ -36,7 +49,7 @@ def k_byte(D, key, c):
 def v_byte(D, key, c):
     G = cfg(D)[0]
     kg, ks = divmod(key, G)
-    return kg * 1024 + (c * G + (ks ^ swV(D, c))) * 16
+    return kg * 1024 + ((c ^ swVc(D, kg)) * G + (ks ^ swVk(D, c))) * 16
 
 
 def bank_ways(addrs, nbytes, banks=64):
@@ -51,7 +64,7 @@ def bank_ways(addrs, nbytes, banks=64):
     return worst
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", DIMS)
 def test_copy_maps_cover_the_tile_once(D):
     G, CPR, BN = cfg(D)
     for name, f in (("K", k_byte), ("V", v_byte)):
@@ -62,21 +75,23 @@ def test_copy_maps_cover_the_tile_once(D):
                 if name == "K":
                     key, c = kg * G + ks_phys, c_phys ^ swK(D, kg)
                 else:
-                    key, c = kg * G + (ks_phys ^ swV(D, c_phys)), c_phys
+                    c = c_phys ^ swVc(D, kg)
+                    key = kg * G + (ks_phys ^ swVk(D, c))
                 assert f(D, key, c) == kg * 1024 + lane * 16
                 seen.add((key, c))
         assert seen == {(k, c) for k in range(BN) for c in range(CPR)}
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", DIMS)
 def test_k_reads_are_immediates_and_conflict_free(D):
     G, CPR, BN = cfg(D)
+    KP = K_BASES[D]
     for t in range(BN // 32):
         for s in range(D // 16):
             addrs = [k_byte(D, 32 * t + l % 32, 2 * s + l // 32) for l in range(64)]
-            base = [k_byte(D, 32 * t + l % 32, 2 * (s % 2) + l // 32) for l in range(64)]
+            base = [k_byte(D, 32 * t + l % 32, 2 * (s % KP) + l // 32) for l in range(64)]
             assert len({a - b for a, b in zip(addrs, base)}) == 1
-            assert addrs[0] - base[0] == (s // 2) * 64 * G
+            assert addrs[0] - base[0] == (s // KP) * 2 * KP * G * 16
             assert bank_ways(addrs, 16) == 1
 
 
@@ -84,26 +99,35 @@ def tr16(sup):
     return [[sup[16 * (L // 16) + 4 * k + (L % 16) // 4][L % 4] for k in range(4)] for L in range(64)]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+def v_read_addrs(D, s, t, half):
+    out = []
+    for L in range(64):
+        q, j = divmod(L, 16)
+        key = 16 * s + 8 * half + 4 * (q // 2) + j // 4
+        d = 32 * t + 16 * (q % 2) + 4 * (j % 4)
+        out.append(v_byte(D, key, d // 8) + (d % 8) * 2)
+    return out
+
+
+@pytest.mark.parametrize("D", DIMS)
 def test_transposing_v_reads_give_p_key_order(D):
     G, CPR, BN = cfg(D)
-    base = None
+    VT, VH = V_BASES[D]
     for s in range(BN // 16):
         for t in range(D // 32):
             got = [[None] * 8 for _ in range(64)]
             for half in range(2):
-                sup, addrs = [], []
+                sup = []
                 for L in range(64):
                     q, j = divmod(L, 16)
                     key = 16 * s + 8 * half + 4 * (q // 2) + j // 4
                     d = 32 * t + 16 * (q % 2) + 4 * (j % 4)
                     sup.append([(key, d + e) for e in range(4)])
-                    addrs.append(v_byte(D, key, d // 8) + (d % 8) * 2)
+                addrs = v_read_addrs(D, s, t, half)
                 assert bank_ways(addrs, 8) == 1
-                if base is None:
-                    base = addrs
+                base = v_read_addrs(D, 0, t % VT, half % VH)
                 off = {a - b for a, b in zip(addrs, base)}
-                assert off == {(16 * s + 8 * half) // G * 1024 + t * 64 * G}
+                assert off == {(16 * s + 8 * (half - half % VH)) // G * 1024 + (t - t % VT) * 64 * G}
                 for L, r in enumerate(tr16(sup)):
                     got[L][4 * half:4 * half + 4] = r
             for L in range(64):

@@ -61,6 +61,18 @@ SMALL = [
     (1, 300, 4, 2, 128, "f32", "causal", -1),
     (1, 275, 4, 4, 64, "f32", "sliding_window", 40),
     (2, 160, 4, 2, 64, "f32", "causal", -1),
+    # head dims 32 and 256
+    (1, 1, 1, 1, 32, "f16", "none", -1),
+    (2, 300, 4, 2, 32, "bf16", "causal", -1),
+    (1, 513, 4, 4, 32, "f16", "none", -1),
+    (1, 400, 4, 1, 32, "bf16", "sliding_window", 77),
+    (1, 300, 4, 2, 32, "f32", "causal", -1),
+    (1, 1, 2, 1, 256, "bf16", "causal", -1),
+    (2, 300, 4, 2, 256, "bf16", "causal", -1),
+    (1, 257, 4, 4, 256, "f16", "none", -1),
+    (1, 400, 4, 2, 256, "bf16", "sliding_window", 100),
+    (1, 300, 4, 2, 256, "f32", "causal", -1),
+    (1, 130, 2, 2, 256, "f32", "sliding_window", 9),
 ]
 
 
@@ -100,7 +112,7 @@ def sample_rows(w, n_heads=6, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("w", inputs.WORKLOADS[1:], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", inputs.WORKLOADS[1:] + inputs.WIDER, ids=lambda w: w.name)
 def test_workload_full_size_sampled_rows(w):
     """Full-size workloads, launched exactly as the benchmark launches them;
     the oracle recomputes a sample of rows one by one."""
@@ -221,7 +233,8 @@ def test_rejects_through_binding():
     assert e.value.status == fa.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64), ("f32", 128)])
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f16", 64), ("f32", 128), ("bf16", 32), ("f16", 256),
+                                  ("f32", 32), ("f32", 256)])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_rows_past_the_end_are_never_used(dt, D, mask):
     """K and V end exactly where NaN-filled memory begins; a ragged last key
