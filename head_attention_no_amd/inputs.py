@@ -13,7 +13,7 @@ that any run reproduces the same bits:
 The named workloads are the five shapes this library is measured and
 checked on: long-context causal and sliding-window attention with grouped
 K/V heads, plus a small fp32 case and a peaked-softmax fp16 case; WIDER adds
-the head dims 32 and 256.
+the head dims 32 and 256 and fp32 at S = 4096.
 """
 from __future__ import annotations
 
@@ -62,11 +62,13 @@ WORKLOADS = [
              k_mult=4.0, seed=1005),
 ]
 
-# Head dims 32 and 256 (the rest of the op's shape contract), sized to the
-# same causal FLOP count as the S = 4096 grouped workload above.
+# The rest of the op's shape contract: head dims 32 and 256, sized to the
+# same causal FLOP count as the S = 4096 grouped workload above, and fp32 at
+# a long sequence.
 WIDER = [
     Workload("mha_b4_s8192_h16_d32_bf16_causal", 4, 8192, 16, 16, 32, "bf16", "causal", seed=1006),
     Workload("mha_b2_s4096_h16_d256_bf16_causal", 2, 4096, 16, 16, 256, "bf16", "causal", seed=1007),
+    Workload("mha_b1_s4096_h16_d128_f32_causal", 1, 4096, 16, 16, 128, "f32", "causal", seed=1008),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS + WIDER}
