@@ -26,7 +26,7 @@ MASKS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding_window": MASK_SLIDIN
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
 # Every symbol that include/fa355.h declares.
-EXPORTS = ("mha_no_cache", "fa355_strerror", "fa355_version", "fa355_plan")
+EXPORTS = ("mha_no_cache", "fa355_strerror", "fa355_version", "fa355_plan", "fa355_topk")
 
 _lib = None
 
@@ -56,6 +56,8 @@ def load(path: str = LIB_PATH):
     ip = ctypes.POINTER(ctypes.c_int)
     lib.fa355_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, i]
     lib.fa355_plan.restype = i
+    lib.fa355_topk.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.fa355_topk.restype = i
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -139,3 +141,35 @@ def attention(q, k, v, scale: float, mask="none", window: int = -1, out=None, st
     if rc != OK:
         raise FA355Error(rc)
     return out
+
+
+def fa355_topk(values, indices, x, B: int, V: int, K: int, stream) -> int:
+    """Raw C-ABI call (device addresses as ints); returns the status code."""
+    return load().fa355_topk(values, indices, x, B, V, K, stream)
+
+
+def topk(x, k: int, values=None, indices=None, stream=None):
+    """The k largest entries of each row of a 2-D float32 device tensor, in
+    descending order, equal values by ascending index: (values, indices),
+    float32 and int32 tensors of shape (rows, k). Launches on ``stream``
+    (default: torch's current stream) without synchronising."""
+    import torch
+
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 2 or x.dtype != torch.float32:
+        raise ValueError("x must be a contiguous 2-D float32 device tensor")
+    B, V = x.shape
+    if values is None:
+        values = torch.empty(B, k, dtype=torch.float32, device=x.device)
+    if indices is None:
+        indices = torch.empty(B, k, dtype=torch.int32, device=x.device)
+    for name, t, dt in (("values", values, torch.float32), ("indices", indices, torch.int32)):
+        if t.shape != (B, k) or t.dtype != dt or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous ({B}, {k}) {dt} tensor on {x.device}")
+    with torch.cuda.device(x.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        rc = fa355_topk(values.data_ptr(), indices.data_ptr(), x.data_ptr(), B, V, int(k),
+                        stream.cuda_stream)
+    if rc != OK:
+        raise FA355Error(rc, "fa355_topk")
+    return values, indices

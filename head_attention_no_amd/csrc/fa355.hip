@@ -14,6 +14,7 @@
 #include "fa355.h"
 #include "mha_fwd16.hpp"
 #include "mha_fwd32.hpp"
+#include "topk.hpp"
 
 namespace {
 
@@ -188,6 +189,35 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     case FA355_F16: err = launch_dim<_Float16>(p, D, mask_kind, grid, s); break;
     default: err = launch_dim<float>(p, D, mask_kind, grid, s); break;
     }
+    return err == hipSuccess ? FA355_OK : FA355_ERR_LAUNCH;
+}
+
+extern "C" int fa355_topk(float *values, int *indices, const float *in, int B, int V, int K,
+                          void *stream)
+{
+    if (!values || !indices || !in) return FA355_ERR_INVALID_ARG;
+    if (B < 1 || V < 1 || K < 1 || K > V) return FA355_ERR_INVALID_ARG;
+    const int64_t in_bytes = (int64_t)B * V * 4, out_bytes = (int64_t)B * K * 4;
+    if (overlaps(values, out_bytes, in, in_bytes) || overlaps(indices, out_bytes, in, in_bytes) ||
+        overlaps(values, out_bytes, indices, out_bytes))
+        return FA355_ERR_INVALID_ARG;
+    if (K > fa355::kTopkMaxK) return FA355_ERR_UNSUPPORTED;
+    if (((reinterpret_cast<uintptr_t>(values) | reinterpret_cast<uintptr_t>(indices) |
+          reinterpret_cast<uintptr_t>(in)) &
+         3u) != 0)
+        return FA355_ERR_UNSUPPORTED;
+    const int rc = check_device();
+    if (rc != FA355_OK) return rc;
+    fa355::TopkParams p;
+    p.values = values;
+    p.indices = indices;
+    p.in = in;
+    p.V = V;
+    p.K = K;
+    void *args[] = {&p};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&fa355::topk_rows), dim3(B),
+                                          dim3(fa355::kTopkThreads), args, 0,
+                                          static_cast<hipStream_t>(stream));
     return err == hipSuccess ? FA355_OK : FA355_ERR_LAUNCH;
 }
 

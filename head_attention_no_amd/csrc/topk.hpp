@@ -1,0 +1,255 @@
+// Top-K ordering of batch rows for gfx950: the top-K token sampler of the
+// recipe page "Custom Operations: Applications in AI Models", section
+// "Optimizing top-K token sampling for GPUs in MAX" (each batch row of
+// next-word frequencies is ordered by highest frequency; one GPU block per
+// row). Result per row: the K largest entries in descending order, equal
+// values by ascending index (-0.0 equals +0.0), as values and indices.
+//
+// One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
+// order keys (larger float, larger key). A radix select over the keys
+// (digits of 12, 12 and 8 bits from the top, histograms in LDS) finds the
+// key prefix of the K-th largest entry and how many entries sharing that
+// prefix must be taken; it stops early once every entry with the prefix is
+// taken. A gather pass then appends the entries above the prefix (in any
+// order) and takes the tied entries in index order (block-wide prefix
+// counts over each chunk of the row); a bitonic sort of the K chosen
+// (key, index) pairs in LDS orders them. The row is read once per radix
+// pass plus once for the gather; everything else stays in LDS.
+#pragma once
+
+#include "mha_common.hpp"
+
+namespace fa355 {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxK = 1024;
+constexpr int kTopkUnroll = 4;  // float4 loads in flight per thread and chunk
+
+struct TopkParams {
+    float *values;
+    int32_t *indices;
+    const float *in;
+    int V, K;
+};
+
+// Order key: unsigned compare of keys = float compare of values; -0.0 and
+// +0.0 get the same key.
+__device__ inline uint32_t order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order; `total`
+// gets the sum over all threads. Uses `scratch` (16 ints of LDS) and two
+// barriers, so every thread must call it.
+__device__ inline int block_exclusive_sum(int v, int *scratch, int &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+        const int s = scratch[w];
+        before += (w < wave) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();  // scratch may be reused right after
+    total = tot;
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
+{
+    __shared__ uint32_t hist[4096];
+    __shared__ uint32_t sel_key[kTopkMaxK];
+    __shared__ int32_t sel_idx[kTopkMaxK];
+    __shared__ int scratch[kTopkThreads / 64];
+    __shared__ int found[2];  // bin, entries still needed within it
+    __shared__ int n_greater;
+
+    const int tid = threadIdx.x;
+    const int V = p.V, K = p.K;
+    const float *x = p.in + (int64_t)blockIdx.x * V;
+
+    // The row as an aligned float4 body between a scalar head and tail.
+    const int head = min(V, (int)(((16u - ((uint32_t)(uintptr_t)x & 15u)) & 15u) >> 2));
+    const int nvec = (V - head) >> 2;
+    const int tail0 = head + 4 * nvec;
+    const float4 *xv = reinterpret_cast<const float4 *>(x + head);
+
+    // Visit every entry (any order): fn(key, index).
+    auto for_each = [&](auto &&fn) {
+        if (tid < head) fn(order_key(x[tid]), tid);
+        for (int i0 = 0; i0 < nvec; i0 += kTopkThreads * kTopkUnroll) {
+            float4 v[kTopkUnroll];
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) {
+                const int j = i0 + u * kTopkThreads + tid;
+                v[u] = j < nvec ? xv[j] : float4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) {
+                const int j = i0 + u * kTopkThreads + tid;
+                if (j < nvec) {
+                    const int e = head + 4 * j;
+                    fn(order_key(v[u].x), e);
+                    fn(order_key(v[u].y), e + 1);
+                    fn(order_key(v[u].z), e + 2);
+                    fn(order_key(v[u].w), e + 3);
+                }
+            }
+        }
+        if (tail0 + tid < V) fn(order_key(x[tail0 + tid]), tail0 + tid);
+    };
+
+    // Radix select. Invariant: the wanted entries are all with
+    // (key & mask) > prefix, plus `need` of those with (key & mask) == prefix.
+    uint32_t prefix = 0u, mask = 0u;
+    int need = K;
+    constexpr int kShift[3] = {20, 8, 0};
+    constexpr int kBits[3] = {12, 12, 8};
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = kShift[pass], nb = 1 << kBits[pass];
+        for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0u;
+        __syncthreads();
+        for_each([&](uint32_t key, int) {
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        // Thread t owns bins top, top-1, .. (descending); the prefix sum in
+        // thread order counts the entries in higher bins.
+        const int bpt = nb >= kTopkThreads ? nb / kTopkThreads : 1;
+        const int top = nb - 1 - tid * bpt;
+        int local = 0;
+        for (int b = 0; b < bpt; ++b)
+            if (top - b >= 0) local += (int)hist[top - b];
+        int total;
+        int above = block_exclusive_sum(local, scratch, total);
+        for (int b = 0; b < bpt; ++b) {
+            if (top - b < 0) break;
+            const int c = (int)hist[top - b];
+            if (above < need && need <= above + c) {
+                found[0] = top - b;
+                found[1] = need - above;
+            }
+            above += c;
+        }
+        __syncthreads();
+        const int bin = found[0];
+        const int left = found[1];
+        const bool all_taken = (int)hist[bin] == left;  // every entry of this bin is wanted
+        prefix |= (uint32_t)bin << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
+        need = left;
+        __syncthreads();  // hist is rewritten by the next pass
+        if (all_taken) break;
+    }
+
+    // Gather: entries above the prefix in any order, ties in index order.
+    if (tid == 0) n_greater = 0;
+    __syncthreads();
+    const int greater = K - need;  // how many entries lie above the prefix
+    int ties_taken = 0;
+    auto take_greater = [&](uint32_t key, int idx) {
+        if ((key & mask) > prefix) {
+            const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
+            if (s < greater) {
+                sel_key[s] = key;
+                sel_idx[s] = idx;
+            }
+        }
+    };
+    // One chunk of up to 4 consecutive entries per thread, chunks in index order.
+    auto chunk = [&](const uint32_t (&key)[4], int idx0, int cnt) {
+        int t = 0;
+        for (int e = 0; e < cnt; ++e) {
+            take_greater(key[e], idx0 + e);
+            t += (key[e] & mask) == prefix;
+        }
+        if (ties_taken < need) {  // uniform
+            int total;
+            int rank = ties_taken + block_exclusive_sum(t, scratch, total);
+            for (int e = 0; e < cnt; ++e)
+                if ((key[e] & mask) == prefix) {
+                    if (rank < need) {
+                        sel_key[greater + rank] = key[e];
+                        sel_idx[greater + rank] = idx0 + e;
+                    }
+                    ++rank;
+                }
+            ties_taken += total;
+        }
+    };
+    {
+        uint32_t k4[4] = {0u, 0u, 0u, 0u};
+        if (tid < head) k4[0] = order_key(x[tid]);
+        chunk(k4, tid, tid < head ? 1 : 0);
+    }
+    for (int i0 = 0; i0 < nvec; i0 += kTopkThreads) {
+        const int j = i0 + tid;
+        uint32_t k4[4] = {0u, 0u, 0u, 0u};
+        int cnt = 0;
+        if (j < nvec) {
+            const float4 v = xv[j];
+            k4[0] = order_key(v.x);
+            k4[1] = order_key(v.y);
+            k4[2] = order_key(v.z);
+            k4[3] = order_key(v.w);
+            cnt = 4;
+        }
+        chunk(k4, head + 4 * j, cnt);
+    }
+    for (int i0 = tail0; i0 < V; i0 += kTopkThreads) {
+        uint32_t k4[4] = {0u, 0u, 0u, 0u};
+        const int i = i0 + tid;
+        if (i < V) k4[0] = order_key(x[i]);
+        chunk(k4, i, i < V ? 1 : 0);
+    }
+    __syncthreads();
+
+    // Bitonic sort of the K pairs by (key descending, index ascending),
+    // padded to a power of two with pairs that sort last.
+    int kp = 1;
+    while (kp < K) kp <<= 1;
+    if (tid >= K && tid < kp) {
+        sel_key[tid] = 0u;
+        sel_idx[tid] = 0x7fffffff;
+    }
+    __syncthreads();
+    for (int size = 2; size <= kp; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int i = tid, j = tid ^ stride;
+            if (i < kp && j > i) {
+                const uint32_t ki = sel_key[i], kj = sel_key[j];
+                const int ii = sel_idx[i], ij = sel_idx[j];
+                const bool i_first = ki > kj || (ki == kj && ii < ij);  // i precedes j
+                const bool ascending_block = (i & size) == 0;            // this block sorts first-to-last
+                if (i_first != ascending_block) {
+                    sel_key[i] = kj;
+                    sel_key[j] = ki;
+                    sel_idx[i] = ij;
+                    sel_idx[j] = ii;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    if (tid < K) {
+        const int idx = sel_idx[tid];
+        p.values[(int64_t)blockIdx.x * K + tid] = x[idx];
+        p.indices[(int64_t)blockIdx.x * K + tid] = idx;
+    }
+}
+
+}  // namespace fa355

@@ -89,3 +89,34 @@ def make_qkv(B: int, S: int, H: int, Hkv: int, D: int, dtype: str = "bf16", seed
 
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.S, w.H, w.Hkv, w.D, w.dtype, w.seed, w.k_mult)
+
+
+# Top-K ordering inputs: rows of next-token scores.
+TOPK_WORKLOAD = {"name": "topk_b256_v128256_k50_f32", "B": 256, "V": 128256, "K": 50,
+                 "kind": "frequencies", "seed": 2001}
+
+
+def make_scores(B: int, V: int, kind: str = "frequencies", seed: int = 0):
+    """Seeded float32 CPU rows (B, V). Kinds: "frequencies" (a softmax of
+    N(0, 3^2) logits, in percent: how often each next token appears),
+    "normal" (N(0,1)), "ties" (multiples of 1/4 in [-1, 1.5]: many equal
+    values), "zeros" (signed zeros with a few negatives), "huge_tiny"
+    (1e30 every third entry, N(0, 1e-30) elsewhere)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    if kind == "frequencies":
+        logits = torch.randn(B, V, generator=g, dtype=torch.float64) * 3.0
+        return (torch.softmax(logits, dim=1) * 100.0).to(torch.float32)
+    if kind == "normal":
+        return torch.randn(B, V, generator=g, dtype=torch.float32)
+    if kind == "ties":
+        return torch.randint(-4, 7, (B, V), generator=g).to(torch.float32) / 4
+    if kind == "zeros":
+        sign = torch.randint(0, 2, (B, V), generator=g).to(torch.bool)
+        x = torch.where(sign, torch.tensor(-0.0), torch.tensor(0.0)).to(torch.float32)
+        x[:, ::97] = -1.0
+        return x
+    if kind == "huge_tiny":
+        x = torch.randn(B, V, generator=g, dtype=torch.float32) * 1e-30
+        x[:, ::3] = 1e30
+        return x
+    raise ValueError(kind)

@@ -123,6 +123,36 @@ const char *fa355_version(void);
 int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups, int *block_m,
                int *block_n, int *tiles, int n);
 
+/*
+ * fa355_topk: the top-K token sampler of the recipe page "Custom
+ * Operations: Applications in AI Models" (builds.modular.com), section
+ * "Optimizing top-K token sampling for GPUs in MAX": each batch row of
+ * next-word frequencies is ordered by highest frequency, and the operation
+ * returns the ordered values and their positions. Here: the K largest
+ * entries of each row in descending order (the page orders the whole row:
+ * K = V), equal values by ascending index, -0.0 equal to +0.0.
+ *
+ * Arguments (device pointers on the current HIP device, contiguous,
+ * 4-byte aligned):
+ *   values   [B, K] float32   written: values[b*K + i] = in[b*V + indices[b*K + i]],
+ *                             bit for bit.
+ *   indices  [B, K] int32     written: positions within the row, 0 .. V-1.
+ *   in       [B, V] float32   read only; finite values (NaN is outside the
+ *                             contract: it is ordered but not tested).
+ *   B, V, K                   rows, entries per row, entries kept per row.
+ *   stream                    a hipStream_t, or NULL for the null stream.
+ * The result is exact and deterministic.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing.
+ * Execution: asynchronous on `stream`.
+ * Errors: FA355_ERR_INVALID_ARG for a null pointer, B, V or K < 1, K > V,
+ * or an output overlapping the input or the other output;
+ * FA355_ERR_UNSUPPORTED for K > 1024 or a pointer not 4-byte aligned;
+ * FA355_ERR_DEVICE / FA355_ERR_LAUNCH as for mha_no_cache. Checks run
+ * before any HIP call.
+ */
+int fa355_topk(float *values, int *indices, const float *in, int B, int V, int K, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

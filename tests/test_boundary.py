@@ -121,3 +121,23 @@ def test_plan_rejects_like_the_entry_point():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         fa.load(str(tmp_path / "libfa355.so"))
+
+
+def topk_call(**over):
+    a = dict(values=P1, indices=P2, x=P3, B=2, V=100, K=10, stream=None)
+    a.update(over)
+    return fa.fa355_topk(a["values"], a["indices"], a["x"], a["B"], a["V"], a["K"], a["stream"])
+
+
+@pytest.mark.parametrize("over", [
+    dict(values=0), dict(indices=0), dict(x=0), dict(B=0), dict(V=0), dict(K=0), dict(K=101),
+    dict(values=P3 + 40), dict(indices=P3 - 4), dict(indices=P1 + 76),
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_topk_invalid_arguments(over):
+    assert topk_call(**over) == fa.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over", [dict(V=5000, K=1025), dict(x=P3 + 2), dict(values=P1 + 1)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_topk_unsupported_arguments(over):
+    assert topk_call(**over) == fa.ERR_UNSUPPORTED

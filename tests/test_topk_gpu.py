@@ -1,0 +1,84 @@
+"""Top-K ordering on the GPU vs the oracle, through the C ABI: bit-exact
+values and indices (the selection is exact integer-like work)."""
+import numpy as np
+import pytest
+import torch
+
+import head_attention_no_amd as fa
+from head_attention_no_amd import inputs
+from oracle import topk as otk
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def run(x, k):
+    vals, idx = fa.topk(x.to(DEV), k)
+    torch.cuda.synchronize()
+    return vals.cpu().numpy(), idx.cpu().numpy()
+
+
+def check(x, k):
+    vals, idx = run(x, k)
+    ov, oi = otk.topk_rows(x.numpy(), k)
+    assert np.array_equal(idx, oi), f"indices differ in rows {np.nonzero((idx != oi).any(1))[0][:5]}"
+    assert np.array_equal(vals.view(np.uint32), ov.view(np.uint32)), "values differ"
+
+
+CASES = [
+    # rows, entries, k, kind
+    (3, 5, 5, "frequencies"),       # the page's demo shape: three rows, whole rows ordered
+    (1, 1, 1, "normal"),
+    (4, 1000, 37, "normal"),
+    (2, 4099, 1024, "normal"),      # ragged row length: rows start at every 16-byte phase
+    (3, 4097, 1, "normal"),
+    (5, 20000, 50, "ties"),
+    (2, 300, 300, "ties"),
+    (3, 777, 100, "zeros"),
+    (2, 129, 64, "huge_tiny"),
+    (64, 50257, 50, "frequencies"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_V{}_K{}_{}".format(*c))
+def test_topk_matches_oracle(case):
+    B, V, k, kind = case
+    note(f"topk case {case}")
+    x = inputs.make_scores(B, V, kind, seed=V + k)
+    check(x, k)
+
+
+def test_topk_full_size_workload():
+    w = inputs.TOPK_WORKLOAD
+    note(f"topk workload {w}")
+    x = inputs.make_scores(w["B"], w["V"], w["kind"], seed=w["seed"])
+    check(x, w["K"])
+
+
+def test_topk_deterministic_and_in_bounds():
+    x = inputs.make_scores(4, 3000, "ties", seed=3).to(DEV)
+    guard = torch.full((4 * 64 + 2048,), -7.0, device=DEV)
+    vals = guard[1024:1024 + 4 * 64].view(4, 64)
+    iguard = torch.full((4 * 64 + 2048,), -7, dtype=torch.int32, device=DEV)
+    idx = iguard[1024:1024 + 4 * 64].view(4, 64)
+    fa.topk(x, 64, values=vals, indices=idx)
+    first = (vals.clone(), idx.clone())
+    fa.topk(x, 64, values=vals, indices=idx)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], vals) and torch.equal(first[1], idx)
+    assert torch.all(guard[:1024] == -7) and torch.all(guard[-1024:] == -7)
+    assert torch.all(iguard[:1024] == -7) and torch.all(iguard[-1024:] == -7)
+
+
+def test_topk_rejects_through_binding():
+    x = torch.zeros(2, 10, device=DEV)
+    with pytest.raises(fa.FA355Error) as e:
+        fa.topk(x, 11)
+    assert e.value.status == fa.ERR_INVALID_ARG
+    with pytest.raises(fa.FA355Error) as e:
+        fa.topk(torch.zeros(2, 2000, device=DEV), 1025)
+    assert e.value.status == fa.ERR_UNSUPPORTED
