@@ -242,6 +242,60 @@ def roofline(w, t):
             "launch_ms_mean": round(t["launch_ms_mean"], 5)}
 
 
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, spec
+
+
+def time_topk(steps: int, warmup: int, with_cpu: bool):
+    """The top-K ordering kernel on its workload (rows of next-token
+    frequencies): HBM-bound, so reported as GB/s of algorithmic traffic
+    (the input read once, values and indices written once) against the HBM
+    peak, plus the oracle on a sample of rows."""
+    import torch
+
+    import head_attention_no_amd as fa
+    from head_attention_no_amd import inputs
+
+    w = inputs.TOPK_WORKLOAD
+    x_cpu = inputs.make_scores(w["B"], w["V"], w["kind"], seed=w["seed"])
+    x = x_cpu.cuda()
+    vals = torch.empty(w["B"], w["K"], device="cuda")
+    idx = torch.empty(w["B"], w["K"], dtype=torch.int32, device="cuda")
+    call = lambda: fa.topk(x, w["K"], values=vals, indices=idx)  # noqa: E731
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        call()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s, e in ev:
+        s.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    nbytes = w["B"] * w["V"] * 4 + w["B"] * w["K"] * 8
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    out = {"workload": w["name"], "launch_ms_mean": round(ms, 5),
+           "rows_per_s": round(w["B"] / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes": nbytes}}
+    if with_cpu:
+        from oracle import topk as otk
+
+        n = 16
+        t0 = time.perf_counter()
+        otk.topk_rows(x_cpu[:n].numpy(), w["K"])
+        sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n / sec, 1), "unit": "rows/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} of {w['B']} rows, numpy lexsort per row, {sec:.2f} s"}
+    return out
+
+
 def one_line(w, args, t, cpu):
     fl = flops(w)
     tflops = fl / (t["ms_per_step"] * 1e-3) / 1e12
@@ -330,6 +384,8 @@ def main():
                 "peak_tflops": PEAK_TFLOPS[o.dtype],
             }
         line["other_workloads"] = others
+        print("# timing top-K ordering", file=sys.stderr, flush=True)
+        line["topk"] = time_topk(args.steps, args.warmup, not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

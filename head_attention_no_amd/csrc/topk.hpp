@@ -6,15 +6,17 @@
 // values by ascending index (-0.0 equals +0.0), as values and indices.
 //
 // One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
-// order keys (larger float, larger key). A radix select over the keys
-// (digits of 12, 12 and 8 bits from the top, histograms in LDS) finds the
-// key prefix of the K-th largest entry and how many entries sharing that
-// prefix must be taken; it stops early once every entry with the prefix is
-// taken. A gather pass then appends the entries above the prefix (in any
-// order) and takes the tied entries in index order (block-wide prefix
-// counts over each chunk of the row); a bitonic sort of the K chosen
-// (key, index) pairs in LDS orders them. The row is read once per radix
-// pass plus once for the gather; everything else stays in LDS.
+// order keys (larger float, larger key). A histogram of the top 12 key bits
+// (in LDS) finds the bin of the K-th largest entry. Usually that bin holds
+// few entries: a second and last read of the row then collects the entries
+// of higher bins and those of the bin itself (candidates, at most 4096)
+// into LDS, where a bitonic sort of the candidates by (key descending,
+// index ascending) picks the ones still needed. When the bin is larger, the
+// radix select continues over the next 12 and 8 bits (stopping once every
+// entry sharing the prefix is wanted), and a gather pass takes the entries
+// above the prefix and the tied entries in index order (block-wide prefix
+// counts over each chunk of the row). Either way a last bitonic sort of the
+// K chosen (key, index) pairs orders them.
 #pragma once
 
 #include "mha_common.hpp"
@@ -24,6 +26,7 @@ namespace fa355 {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkMaxK = 1024;
 constexpr int kTopkUnroll = 4;  // float4 loads in flight per thread and chunk
+constexpr int kTopkCand = 4096;  // LDS room for the entries of the threshold bin
 
 struct TopkParams {
     float *values;
@@ -67,11 +70,40 @@ __device__ inline int block_exclusive_sum(int v, int *scratch, int &total)
     return before + x - v;
 }
 
+// Sort n (a power of two) (key, index) pairs in LDS by key descending, then
+// index ascending; every thread must call it.
+__device__ inline void lds_bitonic_sort(uint32_t *key, int32_t *idx, int n)
+{
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const uint32_t ki = key[i], kj = key[j];
+                    const int ii = idx[i], ij = idx[j];
+                    const bool i_first = ki > kj || (ki == kj && ii < ij);  // i precedes j
+                    const bool forward = (i & size) == 0;  // this block sorts first-to-last
+                    if (i_first != forward) {
+                        key[i] = kj;
+                        key[j] = ki;
+                        idx[i] = ij;
+                        idx[j] = ii;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
 {
     __shared__ uint32_t hist[4096];
     __shared__ uint32_t sel_key[kTopkMaxK];
     __shared__ int32_t sel_idx[kTopkMaxK];
+    __shared__ uint32_t cand_key[kTopkCand];
+    __shared__ int32_t cand_idx[kTopkCand];
+    __shared__ int n_cand;
     __shared__ int scratch[kTopkThreads / 64];
     __shared__ int found[2];  // bin, entries still needed within it
     __shared__ int n_greater;
@@ -117,8 +149,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     int need = K;
     constexpr int kShift[3] = {20, 8, 0};
     constexpr int kBits[3] = {12, 12, 8};
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
+    // One digit: returns how many entries share the new prefix.
+    auto radix_pass = [&](int pass) {
         const int shift = kShift[pass], nb = 1 << kBits[pass];
         for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0u;
         __syncthreads();
@@ -146,79 +178,122 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         }
         __syncthreads();
         const int bin = found[0];
-        const int left = found[1];
-        const bool all_taken = (int)hist[bin] == left;  // every entry of this bin is wanted
+        const int in_bin = (int)hist[bin];
         prefix |= (uint32_t)bin << shift;
         mask |= (uint32_t)(nb - 1) << shift;
-        need = left;
-        __syncthreads();  // hist is rewritten by the next pass
-        if (all_taken) break;
-    }
-
-    // Gather: entries above the prefix in any order, ties in index order.
-    if (tid == 0) n_greater = 0;
-    __syncthreads();
-    const int greater = K - need;  // how many entries lie above the prefix
-    int ties_taken = 0;
-    auto take_greater = [&](uint32_t key, int idx) {
-        if ((key & mask) > prefix) {
-            const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
-            if (s < greater) {
-                sel_key[s] = key;
-                sel_idx[s] = idx;
-            }
-        }
+        need = found[1];
+        __syncthreads();  // hist and found are rewritten by the next pass
+        return in_bin;
     };
-    // One chunk of up to 4 consecutive entries per thread, chunks in index order.
-    auto chunk = [&](const uint32_t (&key)[4], int idx0, int cnt) {
-        int t = 0;
-        for (int e = 0; e < cnt; ++e) {
-            take_greater(key[e], idx0 + e);
-            t += (key[e] & mask) == prefix;
-        }
-        if (ties_taken < need) {  // uniform
-            int total;
-            int rank = ties_taken + block_exclusive_sum(t, scratch, total);
-            for (int e = 0; e < cnt; ++e)
-                if ((key[e] & mask) == prefix) {
-                    if (rank < need) {
-                        sel_key[greater + rank] = key[e];
-                        sel_idx[greater + rank] = idx0 + e;
-                    }
-                    ++rank;
+
+    // Gather of the slow path: entries above the prefix in any order, tied
+    // entries in index order.
+    auto gather_in_order = [&]() {
+        const int greater = K - need;
+        int ties_taken = 0;
+        auto take_greater = [&](uint32_t key, int idx) {
+            if ((key & mask) > prefix) {
+                const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
+                if (s < greater) {
+                    sel_key[s] = key;
+                    sel_idx[s] = idx;
                 }
-            ties_taken += total;
+            }
+        };
+        // One chunk of up to 4 consecutive entries per thread, chunks in index order.
+        auto chunk = [&](const uint32_t (&key)[4], int idx0, int cnt) {
+            int t = 0;
+            for (int e = 0; e < cnt; ++e) {
+                take_greater(key[e], idx0 + e);
+                t += (key[e] & mask) == prefix;
+            }
+            if (ties_taken < need) {  // uniform
+                int total;
+                int rank = ties_taken + block_exclusive_sum(t, scratch, total);
+                for (int e = 0; e < cnt; ++e)
+                    if ((key[e] & mask) == prefix) {
+                        if (rank < need) {
+                            sel_key[greater + rank] = key[e];
+                            sel_idx[greater + rank] = idx0 + e;
+                        }
+                        ++rank;
+                    }
+                ties_taken += total;
+            }
+        };
+        {
+            uint32_t k4[4] = {0u, 0u, 0u, 0u};
+            if (tid < head) k4[0] = order_key(x[tid]);
+            chunk(k4, tid, tid < head ? 1 : 0);
         }
+        for (int i0 = 0; i0 < nvec; i0 += kTopkThreads) {
+            const int j = i0 + tid;
+            uint32_t k4[4] = {0u, 0u, 0u, 0u};
+            int cnt = 0;
+            if (j < nvec) {
+                const float4 v = xv[j];
+                k4[0] = order_key(v.x);
+                k4[1] = order_key(v.y);
+                k4[2] = order_key(v.z);
+                k4[3] = order_key(v.w);
+                cnt = 4;
+            }
+            chunk(k4, head + 4 * j, cnt);
+        }
+        for (int i0 = tail0; i0 < V; i0 += kTopkThreads) {
+            uint32_t k4[4] = {0u, 0u, 0u, 0u};
+            const int i = i0 + tid;
+            if (i < V) k4[0] = order_key(x[i]);
+            chunk(k4, i, i < V ? 1 : 0);
+        }
+        __syncthreads();
     };
-    {
-        uint32_t k4[4] = {0u, 0u, 0u, 0u};
-        if (tid < head) k4[0] = order_key(x[tid]);
-        chunk(k4, tid, tid < head ? 1 : 0);
-    }
-    for (int i0 = 0; i0 < nvec; i0 += kTopkThreads) {
-        const int j = i0 + tid;
-        uint32_t k4[4] = {0u, 0u, 0u, 0u};
-        int cnt = 0;
-        if (j < nvec) {
-            const float4 v = xv[j];
-            k4[0] = order_key(v.x);
-            k4[1] = order_key(v.y);
-            k4[2] = order_key(v.z);
-            k4[3] = order_key(v.w);
-            cnt = 4;
-        }
-        chunk(k4, head + 4 * j, cnt);
-    }
-    for (int i0 = tail0; i0 < V; i0 += kTopkThreads) {
-        uint32_t k4[4] = {0u, 0u, 0u, 0u};
-        const int i = i0 + tid;
-        if (i < V) k4[0] = order_key(x[i]);
-        chunk(k4, i, i < V ? 1 : 0);
+
+    const int in_bin = radix_pass(0);
+    const int greater = K - need;  // how many entries lie above the prefix
+    if (tid == 0) {
+        n_greater = 0;
+        n_cand = 0;
     }
     __syncthreads();
+    if (in_bin <= kTopkCand) {
+        // Second read: entries above the prefix, and the bin's entries as candidates.
+        for_each([&](uint32_t key, int idx) {
+            const uint32_t k = key & mask;
+            if (k > prefix) {
+                const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
+                if (s < greater) {
+                    sel_key[s] = key;
+                    sel_idx[s] = idx;
+                }
+            } else if (k == prefix) {
+                const int s = atomicAdd(&n_cand, 1);  // < in_bin
+                if (s < kTopkCand) {
+                    cand_key[s] = key;
+                    cand_idx[s] = idx;
+                }
+            }
+        });
+        int cp = 1;
+        while (cp < in_bin) cp <<= 1;
+        for (int i = in_bin + tid; i < cp; i += kTopkThreads) {
+            cand_key[i] = 0u;
+            cand_idx[i] = 0x7fffffff;
+        }
+        __syncthreads();
+        lds_bitonic_sort(cand_key, cand_idx, cp);
+        for (int i = tid; i < need; i += kTopkThreads) {
+            sel_key[greater + i] = cand_key[i];
+            sel_idx[greater + i] = cand_idx[i];
+        }
+        __syncthreads();
+    } else {
+        for (int pass = 1; pass < 3; ++pass)
+            if (radix_pass(pass) == need) break;  // every entry sharing the prefix is wanted
+        gather_in_order();
+    }
 
-    // Bitonic sort of the K pairs by (key descending, index ascending),
-    // padded to a power of two with pairs that sort last.
+    // Order the K chosen pairs, padded to a power of two with pairs that sort last.
     int kp = 1;
     while (kp < K) kp <<= 1;
     if (tid >= K && tid < kp) {
@@ -226,24 +301,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         sel_idx[tid] = 0x7fffffff;
     }
     __syncthreads();
-    for (int size = 2; size <= kp; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int i = tid, j = tid ^ stride;
-            if (i < kp && j > i) {
-                const uint32_t ki = sel_key[i], kj = sel_key[j];
-                const int ii = sel_idx[i], ij = sel_idx[j];
-                const bool i_first = ki > kj || (ki == kj && ii < ij);  // i precedes j
-                const bool ascending_block = (i & size) == 0;            // this block sorts first-to-last
-                if (i_first != ascending_block) {
-                    sel_key[i] = kj;
-                    sel_key[j] = ki;
-                    sel_idx[i] = ij;
-                    sel_idx[j] = ii;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    lds_bitonic_sort(sel_key, sel_idx, kp);
 
     if (tid < K) {
         const int idx = sel_idx[tid];

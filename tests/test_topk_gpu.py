@@ -41,6 +41,9 @@ CASES = [
     (3, 777, 100, "zeros"),
     (2, 129, 64, "huge_tiny"),
     (64, 50257, 50, "frequencies"),
+    # threshold bins of more than 4096 entries: the multi-pass path
+    (2, 20000, 100, "zeros"),
+    (2, 50000, 300, "ties"),
 ]
 
 
