@@ -335,6 +335,8 @@ def main():
     ap.add_argument("--yardstick", action="store_true",
                     help="instead, time a large bf16 GEMM and torch's flash attention on the "
                          "workload, for context")
+    ap.add_argument("--topk", action="store_true",
+                    help="instead, time only the top-K ordering kernel on its workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead, time a plain device copy of MIB MiB (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -353,6 +355,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration, args.steps, args.warmup)))
+        return
+    if args.topk:
+        print(json.dumps(time_topk(args.steps, args.warmup, not args.no_cpu_baseline)))
         return
     w = inputs.BY_NAME[args.workload]
     if args.yardstick:
