@@ -6,8 +6,12 @@
 // values by ascending index (-0.0 equals +0.0), as values and indices.
 //
 // One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
-// order keys (larger float, larger key). A histogram of the top 12 key bits
-// (in LDS) finds the bin of the K-th largest entry. Usually that bin holds
+// order keys (larger float, larger key). Long rows first try one read: a
+// histogram of the first 16384 entries bounds the K-th largest key from below, and
+// the one read keeps every entry above the bound as a candidate in LDS
+// (sorted there) unless there are more than 4096. Otherwise a
+// histogram of the top 12 key bits (in LDS) finds the bin of the K-th
+// largest entry of the row. Usually that bin holds
 // few entries: a second and last read of the row then collects the entries
 // of higher bins and those of the bin itself (candidates, at most 4096)
 // into LDS, where a bitonic sort of the candidates by (key descending,
@@ -70,30 +74,62 @@ __device__ inline int block_exclusive_sum(int v, int *scratch, int &total)
     return before + x - v;
 }
 
-// Sort n (a power of two) (key, index) pairs in LDS by key descending, then
-// index ascending; every thread must call it.
+// One compare-exchange of a bitonic network over (key, index) pairs in LDS:
+// pair p of the stage with this stride, in a block of `size` that sorts
+// forward (key descending, then index ascending) when bit `size` of the
+// lower element is clear.
+__device__ inline void bitonic_step(uint32_t *key, int32_t *idx, int p, int stride, int size)
+{
+    const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
+    const int j = i | stride;
+    const uint32_t ki = key[i], kj = key[j];
+    const int ii = idx[i], ij = idx[j];
+    const bool i_first = ki > kj || (ki == kj && ii < ij);  // i precedes j
+    const bool forward = (i & size) == 0;
+    if (i_first != forward) {
+        key[i] = kj;
+        key[j] = ki;
+        idx[i] = ij;
+        idx[j] = ii;
+    }
+}
+
+// Sort n (a power of two, <= 4096) (key, index) pairs in LDS by key
+// descending, then index ascending; every thread must call it. Up to 128
+// elements, one wave sorts them alone, one pair per lane and stage (a
+// wave's LDS accesses complete in order, so no barrier is needed between
+// stages). Above that, wave w owns elements [w n/16, (w+1) n/16): stages
+// whose stride stays inside that slice run per wave without a barrier, and
+// only the few wider stages synchronise the workgroup.
 __device__ inline void lds_bitonic_sort(uint32_t *key, int32_t *idx, int n)
 {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n; i += kTopkThreads) {
-                const int j = i ^ stride;
-                if (j > i) {
-                    const uint32_t ki = key[i], kj = key[j];
-                    const int ii = idx[i], ij = idx[j];
-                    const bool i_first = ki > kj || (ki == kj && ii < ij);  // i precedes j
-                    const bool forward = (i & size) == 0;  // this block sorts first-to-last
-                    if (i_first != forward) {
-                        key[i] = kj;
-                        key[j] = ki;
-                        idx[i] = ij;
-                        idx[j] = ii;
-                    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int npairs = n >> 1;
+    if (n <= 128) {
+        if (wave == 0)
+            for (int size = 2; size <= n; size <<= 1)
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int p = lane; p < npairs; p += 64) bitonic_step(key, idx, p, stride, size);
+                    __builtin_amdgcn_wave_barrier();
                 }
-            }
-            __syncthreads();
-        }
+        __syncthreads();
+        return;
     }
+    const int slice = n / (kTopkThreads / 64);      // elements per wave
+    const int wave_pairs = slice >> 1;
+    for (int size = 2; size <= n; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= slice) {
+                __syncthreads();
+                for (int p = threadIdx.x; p < npairs; p += kTopkThreads) bitonic_step(key, idx, p, stride, size);
+                __syncthreads();
+            } else {
+                for (int p = wave * wave_pairs + lane; p < (wave + 1) * wave_pairs; p += 64)
+                    bitonic_step(key, idx, p, stride, size);
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
@@ -103,7 +139,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     __shared__ int32_t sel_idx[kTopkMaxK];
     __shared__ uint32_t cand_key[kTopkCand];
     __shared__ int32_t cand_idx[kTopkCand];
-    __shared__ int n_cand;
+    __shared__ int n_cand, n_tie;
     __shared__ int scratch[kTopkThreads / 64];
     __shared__ int found[2];  // bin, entries still needed within it
     __shared__ int n_greater;
@@ -149,17 +185,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     int need = K;
     constexpr int kShift[3] = {20, 8, 0};
     constexpr int kBits[3] = {12, 12, 8};
-    // One digit: returns how many entries share the new prefix.
-    auto radix_pass = [&](int pass) {
-        const int shift = kShift[pass], nb = 1 << kBits[pass];
-        for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0u;
-        __syncthreads();
-        for_each([&](uint32_t key, int) {
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
-        });
-        __syncthreads();
-        // Thread t owns bins top, top-1, .. (descending); the prefix sum in
-        // thread order counts the entries in higher bins.
+    // In hist[0 .. nb), the bin holding the want-th largest counted entry:
+    // found[0] = that bin, found[1] = how many of its entries are wanted.
+    // Thread t owns bins top, top-1, .. (descending); the prefix sum in
+    // thread order counts the entries in higher bins.
+    auto find_bin = [&](int nb, int want) {
         const int bpt = nb >= kTopkThreads ? nb / kTopkThreads : 1;
         const int top = nb - 1 - tid * bpt;
         int local = 0;
@@ -170,24 +200,99 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         for (int b = 0; b < bpt; ++b) {
             if (top - b < 0) break;
             const int c = (int)hist[top - b];
-            if (above < need && need <= above + c) {
+            if (above < want && want <= above + c) {
                 found[0] = top - b;
-                found[1] = need - above;
+                found[1] = want - above;
             }
             above += c;
         }
         __syncthreads();
+    };
+    // One digit over the entries `visit` enumerates (fn(key, index) for
+    // each); returns how many of them share the new prefix.
+    auto radix_pass = [&](int pass, auto &&visit) {
+        const int shift = kShift[pass], nb = 1 << kBits[pass];
+        for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0u;
+        __syncthreads();
+        visit([&](uint32_t key, int) {
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        find_bin(nb, need);
         const int bin = found[0];
         const int in_bin = (int)hist[bin];
         prefix |= (uint32_t)bin << shift;
         mask |= (uint32_t)(nb - 1) << shift;
         need = found[1];
-        __syncthreads();  // hist and found are rewritten by the next pass
+        __syncthreads();  // hist and found are rewritten next
         return in_bin;
     };
+    auto visit_row = [&](auto &&fn) { for_each(fn); };
 
-    // Gather of the slow path: entries above the prefix in any order, tied
-    // entries in index order.
+    // From the nc candidates in cand_key/cand_idx, the `want` largest (key
+    // descending, index ascending) go to sel[base .. base + want), in any
+    // order: a radix select over the candidates in LDS, then, if the last
+    // digit still ties, the lowest indices of the tied entries.
+    auto pick = [&](int nc, int base, int want) {
+        auto visit_cand = [&](auto &&fn) {
+            for (int i = tid; i < nc; i += kTopkThreads) fn(cand_key[i], (int)cand_idx[i]);
+        };
+        prefix = 0u;
+        mask = 0u;
+        need = want;
+        int last = 0;
+        for (int pass = 0; pass < 3; ++pass) {
+            last = radix_pass(pass, visit_cand);
+            if (last == need) break;  // every candidate sharing the prefix is wanted
+        }
+        const bool by_index = last != need;  // ties at the full key: lowest indices first
+        const int gt = want - need;
+        if (tid == 0) {
+            n_greater = 0;
+            n_tie = 0;
+        }
+        __syncthreads();
+        int32_t *tie = reinterpret_cast<int32_t *>(hist);
+        visit_cand([&](uint32_t key, int idx) {
+            const uint32_t k = key & mask;
+            if (k > prefix) {
+                const int s = atomicAdd(&n_greater, 1);  // < gt by the select invariant
+                if (s < gt) {
+                    sel_key[base + s] = key;
+                    sel_idx[base + s] = idx;
+                }
+            } else if (k == prefix) {
+                const int s = atomicAdd(&n_tie, 1);  // < last
+                if (!by_index) {
+                    if (s < need) {
+                        sel_key[base + gt + s] = key;
+                        sel_idx[base + gt + s] = idx;
+                    }
+                } else if (s < kTopkCand) {
+                    tie[s] = idx;
+                }
+            }
+        });
+        __syncthreads();
+        if (by_index) {
+            int tp = 1;
+            while (tp < last) tp <<= 1;
+            for (int i = tid; i < tp; i += kTopkThreads) {
+                cand_key[i] = 0u;  // equal keys: the sort orders by index
+                cand_idx[i] = i < last ? tie[i] : 0x7fffffff;
+            }
+            __syncthreads();
+            lds_bitonic_sort(cand_key, cand_idx, tp);
+            for (int i = tid; i < need; i += kTopkThreads) {
+                sel_key[base + gt + i] = prefix;
+                sel_idx[base + gt + i] = cand_idx[i];
+            }
+            __syncthreads();
+        }
+    };
+
+    // Gather of the multi-pass path: entries above the prefix in any
+    // order, tied entries in index order.
     auto gather_in_order = [&]() {
         const int greater = K - need;
         int ties_taken = 0;
@@ -249,48 +354,85 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         __syncthreads();
     };
 
-    const int in_bin = radix_pass(0);
-    const int greater = K - need;  // how many entries lie above the prefix
-    if (tid == 0) {
-        n_greater = 0;
-        n_cand = 0;
-    }
-    __syncthreads();
-    if (in_bin <= kTopkCand) {
-        // Second read: entries above the prefix, and the bin's entries as candidates.
+    bool done = false;
+    // Single-read path for long rows. The bin of the K-th largest entry of
+    // the first chunk (16384 entries) bounds the row's K-th largest from
+    // below, so one read that keeps every entry of that bin or above as a
+    // candidate finds all K. With more than kTopkCand candidates (heavily
+    // tied rows, or a chunk unrepresentative of its row) the two-read path
+    // below runs instead.
+    const int nv0 = min(nvec, 4 * kTopkThreads);
+    if (head + 4 * nv0 >= K && nvec > 2 * nv0) {
+        for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
+        __syncthreads();
+        if (tid < head) atomicAdd(&hist[order_key(x[tid]) >> 20], 1u);
+        for (int j = tid; j < nv0; j += kTopkThreads) {
+            const float4 v = xv[j];
+            atomicAdd(&hist[order_key(v.x) >> 20], 1u);
+            atomicAdd(&hist[order_key(v.y) >> 20], 1u);
+            atomicAdd(&hist[order_key(v.z) >> 20], 1u);
+            atomicAdd(&hist[order_key(v.w) >> 20], 1u);
+        }
+        __syncthreads();
+        find_bin(4096, K);
+        const uint32_t lo = (uint32_t)found[0] << 20;
+        if (tid == 0) n_cand = 0;
+        __syncthreads();
         for_each([&](uint32_t key, int idx) {
-            const uint32_t k = key & mask;
-            if (k > prefix) {
-                const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
-                if (s < greater) {
-                    sel_key[s] = key;
-                    sel_idx[s] = idx;
-                }
-            } else if (k == prefix) {
-                const int s = atomicAdd(&n_cand, 1);  // < in_bin
+            if (key >= lo) {
+                const int s = atomicAdd(&n_cand, 1);
                 if (s < kTopkCand) {
                     cand_key[s] = key;
                     cand_idx[s] = idx;
                 }
             }
         });
-        int cp = 1;
-        while (cp < in_bin) cp <<= 1;
-        for (int i = in_bin + tid; i < cp; i += kTopkThreads) {
-            cand_key[i] = 0u;
-            cand_idx[i] = 0x7fffffff;
+        __syncthreads();
+        const int nc = n_cand;  // >= K: the chunk alone has K entries at or above lo
+        __syncthreads();        // n_cand is reset below
+        if (nc <= kTopkCand) {
+            pick(nc, 0, K);
+            done = true;
+        }
+    }
+
+    if (!done) {
+        // Histogram of the top 12 bits over the whole row.
+        prefix = 0u;
+        mask = 0u;
+        need = K;
+        const int in_bin = radix_pass(0, visit_row);
+        const int greater = K - need;  // how many entries lie above the prefix
+        if (tid == 0) {
+            n_greater = 0;
+            n_cand = 0;
         }
         __syncthreads();
-        lds_bitonic_sort(cand_key, cand_idx, cp);
-        for (int i = tid; i < need; i += kTopkThreads) {
-            sel_key[greater + i] = cand_key[i];
-            sel_idx[greater + i] = cand_idx[i];
+        if (in_bin <= kTopkCand) {
+            // Second read: entries above the prefix, and the bin's entries as candidates.
+            for_each([&](uint32_t key, int idx) {
+                const uint32_t k = key & mask;
+                if (k > prefix) {
+                    const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
+                    if (s < greater) {
+                        sel_key[s] = key;
+                        sel_idx[s] = idx;
+                    }
+                } else if (k == prefix) {
+                    const int s = atomicAdd(&n_cand, 1);  // < in_bin
+                    if (s < kTopkCand) {
+                        cand_key[s] = key;
+                        cand_idx[s] = idx;
+                    }
+                }
+            });
+            __syncthreads();
+            pick(in_bin, greater, need);
+        } else {
+            for (int pass = 1; pass < 3; ++pass)
+                if (radix_pass(pass, visit_row) == need) break;  // every entry sharing the prefix is wanted
+            gather_in_order();
         }
-        __syncthreads();
-    } else {
-        for (int pass = 1; pass < 3; ++pass)
-            if (radix_pass(pass) == need) break;  // every entry sharing the prefix is wanted
-        gather_in_order();
     }
 
     // Order the K chosen pairs, padded to a power of two with pairs that sort last.

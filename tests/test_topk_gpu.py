@@ -41,6 +41,10 @@ CASES = [
     (3, 777, 100, "zeros"),
     (2, 129, 64, "huge_tiny"),
     (64, 50257, 50, "frequencies"),
+    # long rows: the single-read path, and its fallback when the bound admits too many
+    (3, 100003, 200, "normal"),
+    (2, 100003, 10, "ties"),
+    (2, 65536, 1024, "huge_tiny"),
     # threshold bins of more than 4096 entries: the multi-pass path
     (2, 20000, 100, "zeros"),
     (2, 50000, 300, "ties"),
