@@ -205,13 +205,16 @@ def yardsticks(w, steps: int, warmup: int):
     return {"workload": w.name, "yardsticks": out}
 
 
+# Sources of the attention path (the top-K kernel is not part of it).
+ATTENTION_SOURCES = ("fa355.hip", "mha_common.hpp", "mha_fwd16.hpp", "mha_fwd32.hpp")
+
+
 def kernel_sources_hash() -> str:
-    import glob
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "head_attention_no_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, "head_attention_no_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
