@@ -7,7 +7,7 @@
 //
 // One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
 // order keys (larger float, larger key). Long rows first try one read: a
-// histogram of the first 16384 entries bounds the K-th largest key from below, and
+// histogram of the first 8192 entries bounds the K-th largest key from below, and
 // the one read keeps every entry above the bound as a candidate in LDS
 // (sorted there) unless there are more than 4096. Otherwise a
 // histogram of the top 12 key bits (in LDS) finds the bin of the K-th
@@ -31,6 +31,7 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkMaxK = 1024;
 constexpr int kTopkUnroll = 4;  // float4 loads in flight per thread and chunk
 constexpr int kTopkCand = 4096;  // LDS room for the entries of the threshold bin
+constexpr int kTopkChunkVec = 2048;  // float4 vectors in the first chunk (8192 entries)
 
 struct TopkParams {
     float *values;
@@ -355,13 +356,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     };
 
     bool done = false;
-    // Single-read path for long rows. The bin of the K-th largest entry of
-    // the first chunk (16384 entries) bounds the row's K-th largest from
-    // below, so one read that keeps every entry of that bin or above as a
-    // candidate finds all K. With more than kTopkCand candidates (heavily
-    // tied rows, or a chunk unrepresentative of its row) the two-read path
-    // below runs instead.
-    const int nv0 = min(nvec, 4 * kTopkThreads);
+    // Single-read path for rows longer than 16384 entries. The bin of the
+    // K-th largest entry of the first chunk (8192 entries) bounds the row's
+    // K-th largest from below, so one read that keeps every entry of that
+    // bin or above as a candidate finds all K (on 128256-entry frequency
+    // rows with K = 50: about 800 candidates). With more than kTopkCand
+    // candidates (heavily tied rows, or a chunk unrepresentative of its
+    // row) the two-read path below runs instead.
+    const int nv0 = min(nvec, kTopkChunkVec);
     if (head + 4 * nv0 >= K && nvec > 2 * nv0) {
         for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
         __syncthreads();
