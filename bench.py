@@ -19,7 +19,9 @@ import json
 import math
 import os
 import platform
+import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +54,82 @@ def algorithmic_bytes(w) -> int:
 
 
 SETTLE_S = 0.3
+SPEC_SCLK_MHZ = 2400  # shader clock the spec MFMA peak assumes
+
+
+def _gpu_sysfs_dir():
+    """sysfs directory of the first amdgpu device with a shader-clock table."""
+    import glob
+
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        if os.path.isfile(os.path.join(d, "pp_dpm_sclk")):
+            return d
+    return None
+
+
+class ClockSampler:
+    """Samples the shader clock (MHz: the pp_dpm_sclk level marked current)
+    and the socket power (W: hwmon power1_input) from sysfs in a background
+    thread while the GPU runs. Reading sysfs does not touch the GPU's queues.
+    Without those files (not an amdgpu host) it records nothing."""
+
+    def __init__(self, period_s: float = 0.02):
+        self.dir = _gpu_sysfs_dir()
+        self.power_file = self.cap_w = None
+        if self.dir:
+            import glob
+
+            for h in sorted(glob.glob(os.path.join(self.dir, "hwmon", "hwmon*"))):
+                if os.path.isfile(os.path.join(h, "power1_input")):
+                    self.power_file = os.path.join(h, "power1_input")
+                    cap = os.path.join(h, "power1_cap")
+                    if os.path.isfile(cap):
+                        self.cap_w = int(open(cap).read()) / 1e6
+                    break
+        self.period = period_s
+        self.samples = []  # (time.perf_counter(), MHz or None, W or None)
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        mhz = None
+        with open(os.path.join(self.dir, "pp_dpm_sclk")) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*mhz", line, re.I)
+                    mhz = int(m.group(1)) if m else None
+        watts = int(open(self.power_file).read()) / 1e6 if self.power_file else None
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz, watts = self._read()
+            except (OSError, ValueError):
+                return
+            self.samples.append((time.perf_counter(), mhz, watts))
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.dir:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self, t_from: float = 0.0):
+        """Medians over the samples taken at or after t_from, or None."""
+        ss = [x for x in self.samples if x[0] >= t_from]
+        mhz = sorted(x[1] for x in ss if x[1] is not None)
+        watts = sorted(x[2] for x in ss if x[2] is not None)
+        if not mhz:
+            return None
+        return {"sclk_mhz": mhz[len(mhz) // 2],
+                "power_w": round(watts[len(watts) // 2], 1) if watts else None,
+                "power_cap_w": self.cap_w, "samples": len(mhz)}
 
 
 def time_gpu(w, steps: int, warmup: int):
@@ -68,11 +146,16 @@ def time_gpu(w, steps: int, warmup: int):
     # launch back-to-back for SETTLE_S seconds before the counted warmup so
     # the timed steps see the steady state (measured: the first ~40 launches
     # of this kernel run ~12% slower than later ones).
-    t_end = time.perf_counter() + SETTLE_S
+    # The shader clock is sampled over the settled part of that period.
+    sampler = ClockSampler().start()
+    t_start = time.perf_counter()
+    t_end = t_start + SETTLE_S
     while time.perf_counter() < t_end:
         for _ in range(8):
             fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
         torch.cuda.synchronize()
+    sampler.stop()
+    clock = sampler.summary(t_start + SETTLE_S / 3)
     for _ in range(warmup):
         fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
     torch.cuda.synchronize()
@@ -92,6 +175,7 @@ def time_gpu(w, steps: int, warmup: int):
         "launch_ms_mean": sum(launch_ms) / len(launch_ms),
         "launch_ms_median": launch_ms[len(launch_ms) // 2],
         "launch_ms_min": launch_ms[0],
+        "clock": clock,
     }
 
 
@@ -322,8 +406,71 @@ def one_line(w, args, t, cpu):
                    "flop_per_step": fl, "algorithmic_bytes_per_step": algorithmic_bytes(w)},
         "pct_of_mfma_peak": round(100 * tflops / peak, 2),
         "roofline": roofline(w, t),
+        "clock": clock_context(fl, t, peak),
         "cpu_baseline": cpu,
     }
+
+
+def clock_context(fl, t, peak):
+    """The shader clock under this load and the MFMA peak at that clock: the
+    spec peak assumes 2.4 GHz, and the GPU lowers its clock to stay within
+    its power cap."""
+    c = t.get("clock")
+    if not c:
+        return None
+    at = peak * c["sclk_mhz"] / SPEC_SCLK_MHZ
+    achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
+    return dict(c, peak_at_sclk_tflops=round(at, 1), frac_at_sclk=round(achieved / at, 4))
+
+
+def sustained_clocks(names, seconds: float):
+    """Each workload (and a bf16 8192^3 GEMM through torch.matmul) launched
+    back-to-back for `seconds`, with the shader clock and socket power sampled
+    over the last two thirds of the run."""
+    import torch
+
+    import head_attention_no_amd as fa
+    from head_attention_no_amd import inputs
+
+    def run(fn, launches_per_batch):
+        sampler = ClockSampler().start()
+        t0 = time.perf_counter()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            s.record()
+            for _ in range(launches_per_batch):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            n += launches_per_batch
+        sampler.stop()
+        return s.elapsed_time(e) / launches_per_batch, n, sampler.summary(t0 + seconds / 3)
+
+    out = {}
+    for name in names:
+        w = inputs.BY_NAME[name]
+        q, k, v = (x.cuda() for x in inputs.workload_qkv(w))
+        o = torch.empty_like(q)
+        ms, n, c = run(lambda: fa.attention(q, k, v, w.scale, w.mask, w.window, out=o), 20)
+        tf = flops(w) / ms / 1e9
+        out[name] = {"launch_ms": round(ms, 5), "launches": n, "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4), "clock": c}
+        if c:
+            out[name]["frac_at_sclk"] = round(
+                tf / (PEAK_TFLOPS[w.dtype] * c["sclk_mhz"] / SPEC_SCLK_MHZ), 4)
+        del q, k, v, o
+    n3 = 8192
+    a = torch.randn(n3, n3, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n3, n3, device="cuda", dtype=torch.bfloat16)
+    ms, n, c = run(lambda: torch.matmul(a, b), 5)
+    tf = 2 * n3 ** 3 / ms / 1e9
+    out["gemm_bf16_8192"] = {"launch_ms": round(ms, 5), "launches": n, "tflops": round(tf, 1),
+                             "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "clock": c}
+    if c:
+        out["gemm_bf16_8192"]["frac_at_sclk"] = round(
+            tf / (PEAK_TFLOPS["bf16"] * c["sclk_mhz"] / SPEC_SCLK_MHZ), 4)
+    return {"sustained_s": seconds, "results": out}
 
 
 def main():
@@ -340,6 +487,9 @@ def main():
                          "workload, for context")
     ap.add_argument("--topk", action="store_true",
                     help="instead, time only the top-K ordering kernel on its workload")
+    ap.add_argument("--clocks", type=float, default=0.0, metavar="SECONDS",
+                    help="instead, run the workload (with --all: every workload) and a bf16 "
+                         "GEMM back-to-back for SECONDS each, sampling shader clock and power")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead, time a plain device copy of MIB MiB (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -363,6 +513,11 @@ def main():
         print(json.dumps(time_topk(args.steps, args.warmup, not args.no_cpu_baseline)))
         return
     w = inputs.BY_NAME[args.workload]
+    if args.clocks:
+        names = [w.name] + ([o.name for o in inputs.WORKLOADS + inputs.WIDER if o.name != w.name]
+                            if args.all else [])
+        print(json.dumps(sustained_clocks(names, args.clocks)), flush=True)
+        return
     if args.yardstick:
         print(json.dumps(yardsticks(w, args.steps, args.warmup)))
         return
