@@ -54,7 +54,7 @@ def load(path: str = LIB_PATH):
     lib.fa355_version.argtypes = []
     lib.fa355_version.restype = ctypes.c_char_p
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.fa355_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, i]
+    lib.fa355_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip, i]
     lib.fa355_plan.restype = i
     lib.fa355_topk.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.fa355_topk.restype = i
@@ -79,17 +79,19 @@ def version() -> str:
 
 
 def plan(B: int, S: int, H: int, Hkv: int, D: int, dtype: int, with_tiles: bool = False):
-    """Work decomposition: dict(num_workgroups, block_m, block_n[, tiles])."""
+    """Work decomposition: dict(num_workgroups, block_m, block_n,
+    heads_per_workgroup[, tiles]); each tile is (query tile, b, first head)."""
     lib = load()
-    nwg, bm, bn = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    nwg, bm, bn, hp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, ctypes.byref(nwg), ctypes.byref(bm),
-                        ctypes.byref(bn), None, 0)
+                        ctypes.byref(bn), ctypes.byref(hp), None, 0)
     if rc != OK:
         raise FA355Error(rc, "fa355_plan")
-    res = {"num_workgroups": nwg.value, "block_m": bm.value, "block_n": bn.value}
+    res = {"num_workgroups": nwg.value, "block_m": bm.value, "block_n": bn.value,
+           "heads_per_workgroup": hp.value}
     if with_tiles:
         buf = (ctypes.c_int * (3 * nwg.value))()
-        rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, None, None, None, buf, nwg.value)
+        rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, None, None, None, None, buf, nwg.value)
         if rc != OK:
             raise FA355Error(rc, "fa355_plan")
         res["tiles"] = [tuple(buf[3 * w:3 * w + 3]) for w in range(nwg.value)]

@@ -39,19 +39,27 @@ bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
 
 bool supported_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
-// Tile shape of the kernel instance for (dtype, D); D must be supported.
-template <int D>
-int block_m16() { return 32 * fa355::Tile16<D>::NW; }
-int block_m(int dtype, int D)
+// Waves per workgroup of the kernel instance for (dtype, D); D must be supported.
+int waves_per_wg(int dtype, int D)
 {
-    if (dtype == FA355_F32) return fa355::kBlockM32;
+    if (dtype == FA355_F32) return fa355::kWaves32;
     switch (D) {
-    case 32: return block_m16<32>();
-    case 64: return block_m16<64>();
-    case 128: return block_m16<128>();
-    default: return block_m16<256>();
+    case 32: return fa355::Tile16<32>::NW;
+    case 64: return fa355::Tile16<64>::NW;
+    case 128: return fa355::Tile16<128>::NW;
+    default: return fa355::Tile16<256>::NW;
     }
 }
+// Query heads per workgroup: the largest of 8, 4, 2, 1 that divides H / Hkv
+// and does not exceed the workgroup's waves. Those heads share one K/V head.
+int heads_per_wg(int dtype, int D, int rep)
+{
+    for (int hp = 8; hp > 1; hp /= 2)
+        if (hp <= waves_per_wg(dtype, D) && rep % hp == 0) return hp;
+    return 1;
+}
+// Query rows per head in one workgroup (32 per wave).
+int block_m(int dtype, int D, int rep) { return 32 * waves_per_wg(dtype, D) / heads_per_wg(dtype, D, rep); }
 int block_n(int dtype, int D)
 {
     if (dtype == FA355_F32) return fa355::Tile32<64>::BN;
@@ -71,8 +79,9 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     if (dtype != FA355_F32 && dtype != FA355_BF16 && dtype != FA355_F16)
         return FA355_ERR_INVALID_ARG;
     if (!supported_dim(D)) return FA355_ERR_UNSUPPORTED;
-    const int64_t n_qtiles = ((int64_t)S + block_m(dtype, D) - 1) / block_m(dtype, D);
-    if (n_qtiles * B * H > INT32_MAX) return FA355_ERR_UNSUPPORTED;
+    const int rep = H / Hkv;
+    const int64_t n_qtiles = ((int64_t)S + block_m(dtype, D, rep) - 1) / block_m(dtype, D, rep);
+    if (n_qtiles * B * (H / heads_per_wg(dtype, D, rep)) > INT32_MAX) return FA355_ERR_UNSUPPORTED;
     // The 16-bit kernel addresses one (batch, K/V head) slice with 32-bit
     // byte offsets: S rows of Hkv * D elements must stay below 2 GiB.
     if ((int64_t)S * Hkv * D * elem_size(dtype) >= ((int64_t)1 << 31)) return FA355_ERR_UNSUPPORTED;
@@ -170,7 +179,9 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.H = H;
     p.Hkv = Hkv;
     p.rep = H / Hkv;
-    p.n_qtiles = (S + block_m(dtype, D) - 1) / block_m(dtype, D);
+    p.hp = heads_per_wg(dtype, D, p.rep);
+    p.wph = waves_per_wg(dtype, D) / p.hp;
+    p.n_qtiles = (S + 32 * p.wph - 1) / (32 * p.wph);
     p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
@@ -181,7 +192,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     const bool neg = std::signbit(scale) && scale != 0.0f;
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
 
-    const int grid = p.n_qtiles * B * H;
+    const int grid = p.n_qtiles * B * (H / p.hp);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (dtype) {
@@ -230,19 +241,22 @@ extern "C" const char *fa355_strerror(int status)
 extern "C" const char *fa355_version(void) { return "fa355 0.1.0 gfx950"; }
 
 extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups,
-                          int *block_m_out, int *block_n_out, int *tiles, int n)
+                          int *block_m_out, int *block_n_out, int *heads_per_wg_out, int *tiles,
+                          int n)
 {
     const int rc = check_shape(B, S, H, Hkv, D, dtype);
     if (rc != FA355_OK) return rc;
-    const int n_qtiles = (S + block_m(dtype, D) - 1) / block_m(dtype, D);
-    const int grid = n_qtiles * B * H;
+    const int rep = H / Hkv, hp = heads_per_wg(dtype, D, rep), bm = block_m(dtype, D, rep);
+    const int n_qtiles = (S + bm - 1) / bm;
+    const int grid = n_qtiles * B * (H / hp);
     if (num_workgroups) *num_workgroups = grid;
-    if (block_m_out) *block_m_out = block_m(dtype, D);
+    if (block_m_out) *block_m_out = bm;
     if (block_n_out) *block_n_out = block_n(dtype, D);
+    if (heads_per_wg_out) *heads_per_wg_out = hp;
     if (tiles) {
         if (n < 0) return FA355_ERR_INVALID_ARG;
         for (int w = 0; w < n && w < grid; ++w) {
-            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv);
+            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv, hp);
             tiles[3 * w + 0] = c.qt;
             tiles[3 * w + 1] = c.b;
             tiles[3 * w + 2] = c.h;

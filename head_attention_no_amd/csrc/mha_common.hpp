@@ -35,7 +35,9 @@ struct Params {
     const void *v;
     int B, S, H, Hkv;
     int rep;       // H / Hkv: query heads per K/V head
-    int n_qtiles;  // ceil(S / query rows per workgroup)
+    int hp;        // query heads per workgroup: a divisor of rep, so they share one K/V head
+    int wph;       // waves per query head: the workgroup's waves / hp
+    int n_qtiles;  // ceil(S / query rows per head per workgroup)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|
@@ -46,35 +48,42 @@ struct Params {
 // most tiles skip the O rescale altogether.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Workgroup -> (query tile, batch, head). Hardware dispatches workgroup w to
-// XCD w % 8 as that XCD's (w / 8)-th workgroup. When the (batch, K/V head)
-// groups split evenly over the 8 XCDs, every XCD gets whole groups (so the
-// H/Hkv query heads that share K/V also share that XCD's L2) and the same
-// mix of tile lengths; within an XCD, and in the fallback order, the longest
-// query tiles (the last ones, under a causal mask) start first.
+// Workgroup -> (query tile, batch, first head h). A workgroup computes the
+// same query rows of hp consecutive heads h .. h+hp-1, which share one K/V
+// head (hp divides H/Hkv): its waves split as hp heads x (waves / hp) row
+// blocks of 32, and all of them read the one K/V tile in LDS. Packing heads
+// instead of rows keeps a workgroup's rows few, so under a causal or window
+// mask its waves see nearly the same key range and none idles at the
+// per-tile barrier while the others work.
+// Hardware dispatches workgroup w to XCD w % 8 as that XCD's (w / 8)-th
+// workgroup. When the (batch, K/V head) groups split evenly over the 8 XCDs,
+// every XCD gets whole groups (so all the query heads that share K/V also
+// share that XCD's L2) and the same mix of tile lengths; within an XCD, and
+// in the fallback order, the longest query tiles (the last ones, under a
+// causal mask) start first.
 struct TileCoord {
     int qt, b, h;
 };
 
-__host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv)
+__host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv, int hp)
 {
-    const int rep = H / Hkv;
+    const int reps = H / Hkv / hp;  // workgroups per (batch, K/V head) and query tile
     const int groups = B * Hkv;
     TileCoord c;
     if (groups % 8 == 0) {
         const int x = w % 8, slot = w / 8;
-        const int per_tile = (groups / 8) * rep;
+        const int per_tile = (groups / 8) * reps;
         const int qi = slot / per_tile;
         const int rem = slot % per_tile;
-        const int grp = (rem / rep) * 8 + x;
+        const int grp = (rem / reps) * 8 + x;
         c.b = grp / Hkv;
-        c.h = (grp % Hkv) * rep + rem % rep;
+        c.h = ((grp % Hkv) * reps + rem % reps) * hp;
         c.qt = n_qtiles - 1 - qi;
     } else {
-        const int bh = B * H;
+        const int hg = H / hp, bh = B * hg;
         c.qt = n_qtiles - 1 - w / bh;
-        c.b = (w % bh) / H;
-        c.h = w % H;
+        c.b = (w % bh) / hg;
+        c.h = (w % hg) * hp;
     }
     return c;
 }
@@ -107,11 +116,12 @@ __device__ inline bool visible(int row, int key, int S, int W)
     return true;
 }
 
-// Key-tile range [begin, end) a workgroup of BM rows starting at q0 must visit.
-template <int MASK, int BM, int BN>
-__device__ inline void key_tile_range(int q0, int S, int W, int &begin, int &end)
+// Key-tile range [begin, end) a workgroup whose rows (per head) are
+// q0 .. q0+rows-1 must visit.
+template <int MASK, int BN>
+__device__ inline void key_tile_range(int q0, int rows, int S, int W, int &begin, int &end)
 {
-    const int q_last = min(q0 + BM, S) - 1;
+    const int q_last = min(q0 + rows, S) - 1;
     begin = 0;
     end = (S + BN - 1) / BN;
     if (MASK != kMaskNone) end = min(end, q_last / BN + 1);

@@ -8,8 +8,10 @@
 // tile. Scale and mask are applied to the scores before the softmax, as the
 // "FlashAttentionGPU" API page (section "execute", Step 3) specifies.
 //
-// Decomposition: one 4-wave workgroup per (query tile of 128 rows, batch,
-// head); each wave owns 32 query rows; key tiles of BN = 8192 / D keys.
+// Decomposition: one workgroup of NW waves (8, or 4 at D = 256) per
+// (query tile, batch, group of hp heads sharing a K/V head); each wave owns
+// 32 query rows of one head, so a query tile is 32 NW / hp rows; key tiles
+// of BN keys (Tile16 below).
 //
 // Register layouts (32x32x16 MFMA; lane = 0..63, c = lane % 32, g = lane / 32):
 //  * Scores are computed transposed, S^T = K Q^T, so the accumulator column
@@ -156,7 +158,6 @@ void mha_fwd16(Params p)
     using TL = Tile16<D>;
     constexpr int NW = TL::NW;
     constexpr int NTHREADS = 64 * NW;
-    constexpr int BM = 32 * NW;
     constexpr int NCOPY = TL::GROUPS / NW;  // key groups of K (and of V) each wave copies per tile
     constexpr int KP = TL::KP, VT = TL::VT, VH = TL::VH, V_AHEAD = TL::V_AHEAD;
     constexpr int BN = TL::BN;
@@ -172,11 +173,13 @@ void mha_fwd16(Params p)
     const int c32 = lane & 31;
     const int g = lane >> 5;
 
-    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv);
-    const int b = tc.b, h = tc.h, kvh = h / p.rep;
+    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
+    const int b = tc.b, kvh = tc.h / p.rep;
+    const int h = tc.h + wave / p.wph;  // this wave's query head
+    const int rows = 32 * p.wph;        // query rows per head in this workgroup
     const int S = p.S, W = p.window;
-    const int q0 = tc.qt * BM;
-    const int wrow0 = q0 + wave * 32;
+    const int q0 = tc.qt * rows;
+    const int wrow0 = q0 + (wave % p.wph) * 32;
     const int row = wrow0 + c32;  // this lane's query row
 
     const T *__restrict__ Q = static_cast<const T *>(p.q);
@@ -260,7 +263,7 @@ void mha_fwd16(Params p)
     const float sl2e = p.scale_log2;
 
     int kt_begin, kt_end;
-    key_tile_range<MASK, BM, BN>(q0, S, W, kt_begin, kt_end);
+    key_tile_range<MASK, BN>(q0, rows, S, W, kt_begin, kt_end);
 
     constexpr int NPV = BN / 16;  // PV k-steps per tile
     constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step

@@ -2,8 +2,9 @@
 // register layouts as the 16-bit kernel (mha_fwd16.hpp), on the fp32 matrix
 // cores (v_mfma_f32_32x32x2_f32), so no input is ever rounded below fp32.
 //
-// One 4-wave workgroup per (query tile of 128 rows, batch, head); each wave
-// owns 32 query rows; key tiles of 32 keys.
+// One 4-wave workgroup per (query tile, batch, group of hp heads sharing a
+// K/V head); each wave owns 32 query rows of one head, so a query tile is
+// 128 / hp rows; key tiles of 32 keys.
 //  * S^T = K Q^T: for k-step s (0 .. D/2-1) lane (c, g) supplies
 //    Q[row c][dsel(s, g)] and K[key c][dsel(s, g)], dsel(s, g) =
 //    s%H + 2H(s/H) + Hg with H = min(32, D/2) (any split of d between the
@@ -22,7 +23,7 @@
 namespace fa355 {
 
 constexpr int kThreads32 = 256;  // 4 waves of 64 lanes
-constexpr int kBlockM32 = 128;   // query rows per workgroup (32 per wave)
+constexpr int kWaves32 = kThreads32 / 64;  // 32 query rows each
 
 template <int D>
 struct Tile32 {
@@ -50,15 +51,17 @@ void mha_fwd32(Params p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int c32 = lane & 31;
     const int g = lane >> 5;
 
-    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv);
-    const int b = tc.b, h = tc.h, kvh = h / p.rep;
+    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
+    const int b = tc.b, kvh = tc.h / p.rep;
+    const int h = tc.h + wave / p.wph;  // this wave's query head
+    const int rows = 32 * p.wph;        // query rows per head in this workgroup
     const int S = p.S, W = p.window;
-    const int q0 = tc.qt * kBlockM32;
-    const int wrow0 = q0 + wave * 32;
+    const int q0 = tc.qt * rows;
+    const int wrow0 = q0 + (wave % p.wph) * 32;
     const int row = wrow0 + c32;  // this lane's query row
 
     const float *__restrict__ Q = static_cast<const float *>(p.q);
@@ -85,7 +88,7 @@ void mha_fwd32(Params p)
     }
 
     int kt_begin, kt_end;
-    key_tile_range<MASK, kBlockM32, BN>(q0, S, W, kt_begin, kt_end);
+    key_tile_range<MASK, BN>(q0, rows, S, W, kt_begin, kt_end);
 
     // Staging: every thread moves D/32 rows x 16 bytes of K and of V.
     constexpr int CPR = D / 4;

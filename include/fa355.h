@@ -112,16 +112,20 @@ const char *fa355_version(void);
 
 /*
  * Work decomposition of one mha_no_cache call, for inspection and tests;
- * pure host arithmetic, no HIP call. Given the call's shape, reports the
- * number of workgroups and, for each of the first `n` workgroup indices,
- * which (query tile, batch, head) it computes: tiles[3*w + 0] = query tile
- * (rows tile*block_m ... tile*block_m + block_m - 1), tiles[3*w + 1] = b,
- * tiles[3*w + 2] = h. `tiles` may be NULL to query only the sizes.
+ * pure host arithmetic, no HIP call. A workgroup computes the same block_m
+ * query rows of heads_per_wg consecutive query heads, which share one K/V
+ * head (heads_per_wg is the largest of 8, 4, 2, 1 that divides H / Hkv and
+ * fits the kernel's waves), against key tiles of block_n keys. Given the
+ * call's shape, reports the number of workgroups and, for each of the first
+ * `n` workgroup indices, what it computes: tiles[3*w + 0] = query tile (rows
+ * tile*block_m ... tile*block_m + block_m - 1), tiles[3*w + 1] = b,
+ * tiles[3*w + 2] = first head h (heads h ... h + heads_per_wg - 1). Any
+ * output pointer may be NULL; `tiles` NULL queries only the sizes.
  * Returns FA355_OK or FA355_ERR_INVALID_ARG / FA355_ERR_UNSUPPORTED under
  * the same rules as mha_no_cache.
  */
 int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups, int *block_m,
-               int *block_n, int *tiles, int n);
+               int *block_n, int *heads_per_wg, int *tiles, int n);
 
 /*
  * fa355_topk: the top-K token sampler of the recipe page "Custom

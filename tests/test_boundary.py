@@ -70,28 +70,35 @@ def test_unsupported_arguments(over):
 
 
 @pytest.mark.parametrize("shape", [
-    (2, 4096, 32, 8, 128, fa.BF16),   # (batch, K/V head) groups split over the 8 XCDs
-    (4, 2048, 32, 32, 128, fa.BF16),
+    (2, 4096, 32, 8, 128, fa.BF16),   # (batch, K/V head) groups split over the 8 XCDs; 4 heads packed
+    (4, 2048, 32, 32, 128, fa.BF16),  # MHA: one head per workgroup
     (1, 8192, 32, 8, 128, fa.BF16),
     (1, 16384, 16, 16, 64, fa.F16),
     (1, 128, 4, 4, 64, fa.F32),       # 4 groups: fallback order
-    (3, 300, 6, 2, 64, fa.BF16),      # ragged S, 6 groups
+    (3, 300, 6, 2, 64, fa.BF16),      # ragged S, 3 heads per K/V head: no packing
     (1, 1, 1, 1, 128, fa.F16),
-    (2, 1000, 8, 2, 32, fa.BF16),
-    (1, 777, 8, 8, 256, fa.F16),      # 128-row tiles at D = 256
-    (1, 300, 4, 2, 256, fa.F32),
+    (2, 1000, 8, 2, 32, fa.BF16),     # 4 heads per K/V head
+    (1, 777, 8, 8, 256, fa.F16),      # 4-wave workgroups at D = 256
+    (1, 300, 4, 2, 256, fa.F32),      # 2 heads packed into a 4-wave workgroup
+    (2, 500, 16, 1, 64, fa.BF16),     # 16 heads per K/V head: 8 packed (one per wave)
+    (1, 640, 32, 4, 128, fa.F32),     # 8 heads per K/V head, 4-wave workgroups: 4 packed
+    (2, 96, 12, 6, 256, fa.BF16),     # 2 packed at D = 256
 ])
 def test_plan_covers_every_tile_once(shape):
     B, S, H, Hkv, D, dt = shape
     pl = fa.plan(B, S, H, Hkv, D, dt, with_tiles=True)
-    nq = -(-S // pl["block_m"])
-    assert pl["block_m"] == (128 if dt == fa.F32 or D == 256 else 256)
+    waves = 4 if dt == fa.F32 or D == 256 else 8
+    hp = max(x for x in (1, 2, 4, 8) if x <= waves and (H // Hkv) % x == 0)
+    assert pl["heads_per_workgroup"] == hp
+    assert pl["block_m"] == 32 * waves // hp
     assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 128, 128: 64, 256: 32}[D])
-    assert pl["num_workgroups"] == nq * B * H
+    nq = -(-S // pl["block_m"])
+    assert pl["num_workgroups"] == nq * B * H // hp
     tiles = pl["tiles"]
-    assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B) for h in range(H))
+    assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B)
+                                   for h in range(0, H, hp))
     # Longest (last) query tiles are dispatched first.
-    first = tiles[:min(len(tiles), B * H)]
+    first = tiles[:min(len(tiles), B * H // hp)]
     assert all(t == nq - 1 for t, _, _ in first)
 
 

@@ -73,6 +73,14 @@ SMALL = [
     (1, 400, 4, 2, 256, "bf16", "sliding_window", 100),
     (1, 300, 4, 2, 256, "f32", "causal", -1),
     (1, 130, 2, 2, 256, "f32", "sliding_window", 9),
+    # several query heads per workgroup (they share one K/V head)
+    (2, 333, 16, 1, 64, "bf16", "causal", -1),              # 8 heads packed, 32 rows each
+    (1, 200, 8, 1, 64, "f32", "causal", -1),                # 4 packed in the fp32 kernel
+    (1, 300, 8, 2, 256, "bf16", "sliding_window", 60),      # 4 packed at D = 256
+    (1, 257, 4, 2, 32, "f16", "sliding_window", 31),        # 2 packed at D = 32
+    (1, 1000, 8, 1, 128, "bf16", "sliding_window", 200),    # 8 packed, window
+    (1, 400, 12, 2, 128, "bf16", "causal", -1),             # 6 per K/V head: 2 packed
+    (3, 33, 8, 2, 128, "f16", "none", -1),                  # S below one 64-row tile
 ]
 
 
