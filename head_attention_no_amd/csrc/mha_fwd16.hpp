@@ -78,6 +78,17 @@ struct Tile16 {
     static constexpr int VT = D == 256 ? 2 : 1;   // V read bases per 32-dim sub-tile period
     static constexpr int VH = D == 32 ? 2 : 1;    // V read bases per 8-key half period
     static constexpr int V_AHEAD = 2 * ND <= 8 ? 2 : 1;  // PV k-steps whose V reads are in flight
+    // Software-pipelined key loop (the next tile's S MFMAs interleaved with
+    // this tile's softmax, then its PV MFMAs with the next tile's max), in an
+    // issue order fixed at compile time. Measured faster at D = 64 (1 %-2 %)
+    // and D = 256 (one wave per SIMD, so no second wave hides the softmax:
+    // 17 %), slower at D = 32 (bound by the vector units) and D = 128 (held at
+    // the power cap, where the extra S MFMAs of each wave's last tile cost
+    // more than the overlap gains).
+    static constexpr bool PIPELINE = D == 64 || D == 256;
+    static constexpr int PIPE_K_AHEAD = 3;    // K operand reads issued this many MFMAs ahead
+    static constexpr int PIPE_V_AHEAD = 4;    // V operand pairs issued this many MFMAs ahead
+    static constexpr int PIPE_MAX_DELAY = 3;  // MFMAs between the last S MFMA and its max
     static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
     static_assert(GROUPS % NW == 0, "every wave copies the same number of key groups");
 };
@@ -138,6 +149,24 @@ __device__ inline void lds_wait(u32x2 (&r)[N])
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(PENDING) : "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// 16-byte LDS read at byte address addr + OFF, as inline asm for the same
+// reason as lds_read_tr16, waited for with lds_wait4().
+template <int OFF>
+__device__ inline u32x4 lds_read_b128(uint32_t addr)
+{
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+
+template <int PENDING>
+__device__ inline void lds_wait4(u32x4 &r)
+{
+    static_assert(PENDING >= 0 && PENDING <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(PENDING) : "memory");
+    asm volatile("" : "+v"(r));
 }
 
 __device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds_dst, uint32_t voffset)
@@ -265,116 +294,373 @@ void mha_fwd16(Params p)
     int kt_begin, kt_end;
     key_tile_range<MASK, BN>(q0, rows, S, W, kt_begin, kt_end);
 
-    constexpr int NPV = BN / 16;  // PV k-steps per tile
-    constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step
+    if constexpr (TL::PIPELINE) {
+        constexpr int NPV = BN / 16;    // PV k-steps per tile
+        constexpr int NSM = D / 16 * NKT;  // S MFMAs per tile
+        constexpr int NPM = NPV * ND;   // PV MFMAs per tile
+        constexpr int NM = NSM + NPM;   // MFMAs per step
+        constexpr int NPAIR = 4 * NPV;  // score pairs per lane per tile
+        constexpr int KA = TL::PIPE_K_AHEAD, VA = TL::PIPE_V_AHEAD, MD = TL::PIPE_MAX_DELAY;
 
-    __syncthreads();  // LDS zeroed before the first copy lands
-    copy_tile(kt_begin, 0);
-    land_tile(0);
-    __syncthreads();
-
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int stage = (kt - kt_begin) & 1;
-        if (kt + 1 < kt_end) copy_tile(kt + 1, stage ^ 1);
-
-        const int k0 = kt * BN;
-        const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
-        if (cls != kEmpty) {
-            const uint8_t *Ks = lds + stage * TL::STAGE_BYTES;
-
-            // S^T = K Q^T.
-            f32x16 sacc[NKT];
+        // Per-lane LDS read bases; the stage and k-step offsets are immediates.
+        uint32_t kb[NKT][KP];
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) sacc[t] = f32x16{};
+        for (int t = 0; t < NKT; ++t)
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s)
+            for (int q = 0; q < KP; ++q) kb[t][q] = lds_base + k_addr[t][q];
+        uint32_t vb[VT][VH];
 #pragma unroll
-                for (int t = 0; t < NKT; ++t) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                        Ks + k_addr[t][s % KP] + (s / KP) * 2 * KP * G * 16);
-                    sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
+        for (int tb = 0; tb < VT; ++tb)
+#pragma unroll
+            for (int hb = 0; hb < VH; ++hb) vb[tb][hb] = lds_base + v_addr[tb][hb];
+
+        // K and V of a tile are copied one step apart: K(kt) goes to stage
+        // (kt - kt_begin) & 1 one step before V(kt) goes to the same stage.
+        auto copy_k = [&](int kt, int stage) {
+            const __amdgpu_buffer_rsrc_t rk = tile_rsrc(Kbh, kt);
+            uint8_t *kdst = lds + stage * TL::STAGE_BYTES;
+#pragma unroll
+            for (int n = 0; n < NCOPY; ++n) lds_copy16(rk, kdst + (wave + NW * n) * 1024, voff_k[n]);
+        };
+        auto copy_v = [&](int kt, int stage) {
+            const __amdgpu_buffer_rsrc_t rv = tile_rsrc(Vbh, kt);
+            uint8_t *vdst = lds + stage * TL::STAGE_BYTES + TL::TILE_BYTES;
+#pragma unroll
+            for (int n = 0; n < NCOPY; ++n) lds_copy16(rv, vdst + (wave + NW * n) * 1024, voff_v[n]);
+        };
+        auto cls_of = [&](int kt) {
+            return kt < kt_end ? classify<MASK>(wrow0, kt * BN, kt * BN + BN - 1, S, W) : (int)kEmpty;
+        };
+        auto mask_tile = [&](f32x16 (&sc)[NKT], int k0) {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+                    if (!visible<MASK>(row, key, S, W)) sc[t][r] = -INFINITY;
                 }
-
-            // Edge tiles only: hidden scores become -inf, so exp2 gives them
-            // exactly 0 below (the scale is never below 1e-30).
-            if (cls == kEdge) {
-#pragma unroll
-                for (int t = 0; t < NKT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
-                    }
-            }
-
-            // V^T operands: the reads for PV k-steps s .. s+V_AHEAD-1 are in
-            // flight while the exponentials of step s are computed.
-            const uint32_t v_region = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES;
-            uint32_t v_stage[VT][VH];
-#pragma unroll
-            for (int tb = 0; tb < VT; ++tb)
-#pragma unroll
-                for (int hb = 0; hb < VH; ++hb) v_stage[tb][hb] = v_region + v_addr[tb][hb];
-            u32x2 vr[NPV][NVR];
-            auto issue_v = [&](auto s_tag) {
-                constexpr int s = decltype(s_tag)::value;
-                if constexpr (s < NPV) {
-                    static_for<ND>([&](auto t_tag) {
-                        constexpr int t = decltype(t_tag)::value;
-                        constexpr int toff = (t - t % VT) * 64 * G;
-                        constexpr int lo = (16 * s) / G * 1024 + toff;
-                        constexpr int hi = (16 * s + 8 * (1 - 1 % VH)) / G * 1024 + toff;
-                        vr[s][2 * t] = lds_read_tr16<lo>(v_stage[t % VT][0]);
-                        vr[s][2 * t + 1] = lds_read_tr16<hi>(v_stage[t % VT][1 % VH]);
-                    });
-                }
-            };
-            static_for<V_AHEAD>(issue_v);
-
-            // Running max; raised (and O, l rescaled) only when it grows by
-            // more than 2^kRescaleLog2.
+        };
+        auto tile_max = [&](f32x16 (&sc)[NKT]) {
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-            const float mt = half_max(mx) * sl2e;
-            if (wave_any(mt > m_run + kRescaleLog2)) {
-                const float m_new = fmaxf(m_run, mt);
-                const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int t = 0; t < ND; ++t) oacc[t] *= alpha;
-                m_run = m_new;
-            }
-            const float base = (m_run == -INFINITY) ? 0.0f : m_run;
-
-            // P = exp2(s * scale log2e - m), rounded to T; l += sum of the
-            // rounded values; O^T += V^T P^T.
-            static_for<NPV>([&](auto s_tag) {
-                constexpr int s = decltype(s_tag)::value;
-                constexpr int o8 = 8 * (s & 1);
-                u32x4 pb;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e0 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i], sl2e, -base));
-                    const float e1 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i + 1], sl2e, -base));
-                    pb[i] = pack2<T>(e0, e1);
-                    l_run = sum2<T>(pb[i], l_run);
-                }
-                lds_wait<(V_AHEAD > 1 && s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
-#pragma unroll
-                for (int t = 0; t < ND; ++t) {
-                    const u32x4 a = {vr[s][2 * t][0], vr[s][2 * t][1], vr[s][2 * t + 1][0],
-                                     vr[s][2 * t + 1][1]};
-                    oacc[t] = mfma16<T>(a, pb, oacc[t]);
-                }
-                issue_v(std::integral_constant<int, s + V_AHEAD>{});
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+            return half_max(mx) * sl2e;
+        };
+        // Operand of S MFMA m (k-step m / NKT, sub-tile m % NKT) from stage PAR.
+        auto k_read = [&](auto par_tag, auto m_tag) {
+            constexpr int PAR = decltype(par_tag)::value, m = decltype(m_tag)::value;
+            constexpr int s = m / NKT, t = m % NKT;
+            return lds_read_b128<PAR * TL::STAGE_BYTES + (s / KP) * 2 * KP * G * 16>(kb[t][s % KP]);
+        };
+        // The two transposing reads for PV MFMA j (k-step j / ND, 32-dim sub-tile j % ND) from stage PAR.
+        auto v_read = [&](auto par_tag, auto j_tag, u32x2 (&dst)[2]) {
+            constexpr int PAR = decltype(par_tag)::value, j = decltype(j_tag)::value;
+            constexpr int s = j / ND, t = j % ND;
+            constexpr int base = PAR * TL::STAGE_BYTES + TL::TILE_BYTES + (t - t % VT) * 64 * G;
+            dst[0] = lds_read_tr16<base + (16 * s) / G * 1024>(vb[t % VT][0]);
+            dst[1] = lds_read_tr16<base + (16 * s + 8 * (1 - 1 % VH)) / G * 1024>(vb[t % VT][1 % VH]);
+        };
+        // S = K Q^T of the first tile, not interleaved.
+        auto s_only = [&](auto par_tag, f32x16 (&sc)[NKT]) {
+            constexpr int AH = NSM < 4 ? NSM : 4;  // reads in flight
+            u32x4 kr[NSM];
+            static_for<AH>([&](auto m_tag) { kr[m_tag] = k_read(par_tag, m_tag); });
+            static_for<NSM>([&](auto m_tag) {
+                constexpr int m = decltype(m_tag)::value;
+                lds_wait4<(m + AH <= NSM ? AH : NSM - m) - 1>(kr[m]);
+                sc[m % NKT] = mfma16<T>(kr[m], qf[m / NKT], m < NKT ? f32x16{} : sc[m % NKT]);
+                if constexpr (m + AH < NSM) kr[m + AH] = k_read(par_tag, std::integral_constant<int, m + AH>{});
             });
-        }
+        };
 
-        if (kt + 1 < kt_end) land_tile(stage ^ 1);  // this wave's part of the next tile
-        __syncthreads();  // ... and everyone's; the current stage is free again
+        // Issue plan of one step, fixed at compile time. Slot p holds what is
+        // issued right after MFMA p (p = -1: before MFMA 0); MFMAs 0 .. NSM-1 are
+        // the next tile's S, then NPM PV MFMAs of this tile.
+        //  - K operand m is read in slot m - KA, V operand pair j in slot NSM + j - VA;
+        //  - score pair j (fma, exp2, pack, row sum) is computed in slot
+        //    j NSM / NPAIR - 1, one per S MFMA at D = 128 and 256, and at the latest
+        //    in the slot before the PV MFMAs that consume it;
+        //  - the next tile's row max is folded 4 values per slot from slot NSM + MD,
+        //    once its S MFMAs have completed.
+        constexpr auto k_slot = [](int m) { return m - KA < -1 ? -1 : m - KA; };
+        constexpr auto v_slot = [](int j) { return NSM + j - VA < -1 ? -1 : NSM + j - VA; };
+        constexpr auto pair_slot = [](int j) {
+            const int e = j * NSM / NPAIR - 1;
+            const int deadline = NSM + (j / 4) * ND - 1;
+            return e < deadline ? e : deadline;
+        };
+        constexpr auto reads_in_slot = [k_slot, v_slot](int p) {
+            int n = 0;
+            for (int m = 0; m < NSM; ++m) n += k_slot(m) == p;
+            for (int j = 0; j < NPM; ++j) n += 2 * (v_slot(j) == p);
+            return n;
+        };
+        // LDS reads (this wave's, in issue order) still allowed in flight when an
+        // MFMA waits for its operand: those issued after it.
+        constexpr auto k_pending = [k_slot, v_slot, reads_in_slot](int m) {
+            const int p = k_slot(m);
+            int n = 0;
+            for (int m2 = m + 1; m2 < NSM; ++m2) n += k_slot(m2) == p;
+            for (int j = 0; j < NPM; ++j) n += 2 * (v_slot(j) == p);
+            for (int q = p + 1; q <= m - 1; ++q) n += reads_in_slot(q);
+            return n;
+        };
+        constexpr auto v_pending = [v_slot, reads_in_slot](int j) {
+            const int p = v_slot(j);
+            int n = 0;
+            for (int j2 = j + 1; j2 < NPM; ++j2) n += 2 * (v_slot(j2) == p);
+            for (int q = p + 1; q <= NSM + j - 1; ++q) n += reads_in_slot(q);
+            return n;
+        };
+
+        // One step: softmax and PV of tile kt (scores `cur`, V in stage PAR) with
+        // S of tile kt+1 (into `nxt`, K in stage PAR ^ 1) interleaved; returns the
+        // next tile's scaled row max. A tile hidden from the whole wave runs with
+        // base = +inf, so every P is 0 (its scores must be finite).
+        auto body = [&](auto par_tag, f32x16 (&cur)[NKT], f32x16 (&nxt)[NKT], bool hidden) {
+            constexpr int PAR = decltype(par_tag)::value;
+            const float base = hidden ? INFINITY : (m_run == -INFINITY) ? 0.0f : m_run;
+            u32x4 kr[NSM];
+            u32x2 vr[NPM][2];
+            uint32_t pb[NPAIR];
+            float mxa = -INFINITY, mxb = -INFINITY;
+            auto issue_reads = [&](auto p_tag) {
+                constexpr int p = decltype(p_tag)::value;
+                static_for<NSM>([&](auto m_tag) {
+                    if constexpr (k_slot(decltype(m_tag)::value) == p)
+                        kr[m_tag] = k_read(std::integral_constant<int, PAR ^ 1>{}, m_tag);
+                });
+                static_for<NPM>([&](auto j_tag) {
+                    if constexpr (v_slot(decltype(j_tag)::value) == p) v_read(par_tag, j_tag, vr[j_tag]);
+                });
+            };
+            auto slot_valu = [&](auto p_tag) {
+                constexpr int p = decltype(p_tag)::value;
+                static_for<NPAIR>([&](auto j_tag) {
+                    constexpr int j = decltype(j_tag)::value;
+                    if constexpr (pair_slot(j) == p) {
+                        constexpr int s = j / 4, i = j % 4, o8 = 8 * (s & 1);
+                        const float e0 = exp2_fast(fmaf(cur[s >> 1][o8 + 2 * i], sl2e, -base));
+                        const float e1 = exp2_fast(fmaf(cur[s >> 1][o8 + 2 * i + 1], sl2e, -base));
+                        pb[j] = pack2<T>(e0, e1);
+                        l_run = sum2<T>(pb[j], l_run);
+                    }
+                });
+                if constexpr (p >= NSM + MD && 4 * (p - NSM - MD) < 16 * NKT) {
+                    constexpr int r0 = 4 * (p - NSM - MD);
+#pragma unroll
+                    for (int r = r0; r < r0 + 4; r += 2) {
+                        mxa = fmaxf(mxa, nxt[r / 16][r % 16]);
+                        mxb = fmaxf(mxb, nxt[r / 16][r % 16 + 1]);
+                    }
+                }
+            };
+
+            issue_reads(std::integral_constant<int, -1>{});
+            slot_valu(std::integral_constant<int, -1>{});
+            static_for<NM>([&](auto m_tag) {
+                constexpr int m = decltype(m_tag)::value;
+                if constexpr (m < NSM) {
+                    lds_wait4<k_pending(m)>(kr[m]);
+                    nxt[m % NKT] = mfma16<T>(kr[m], qf[m / NKT], m < NKT ? f32x16{} : nxt[m % NKT]);
+                } else {
+                    constexpr int j = m - NSM, s = j / ND, t = j % ND;
+                    lds_wait<v_pending(j)>(vr[j]);
+                    const u32x4 a = {vr[j][0][0], vr[j][0][1], vr[j][1][0], vr[j][1][1]};
+                    const u32x4 b = {pb[4 * s], pb[4 * s + 1], pb[4 * s + 2], pb[4 * s + 3]};
+                    oacc[t] = mfma16<T>(a, b, oacc[t]);
+                }
+                issue_reads(m_tag);
+                slot_valu(m_tag);
+            });
+            // The part of the max the slots did not cover.
+            constexpr int done = NPM > MD ? 4 * (NPM - MD) : 0;
+#pragma unroll
+            for (int r = done < 16 * NKT ? done : 16 * NKT; r < 16 * NKT; r += 2) {
+                mxa = fmaxf(mxa, nxt[r / 16][r % 16]);
+                mxb = fmaxf(mxb, nxt[r / 16][r % 16 + 1]);
+            }
+            return half_max(fmaxf(mxa, mxb)) * sl2e;
+        };
+
+        // Step for tile kt at stage parity PAR = (kt - kt_begin) & 1: copies of
+        // K(kt+2) and V(kt+1), then the body. The next tile's S is computed even
+        // when it is hidden from this wave (or lies past the end: stale but finite
+        // LDS data), so the common path has no branch around MFMA work; its max is
+        // then discarded.
+        int cls_cur = cls_of(kt_begin);
+        float mt = -INFINITY;  // scaled row max of the current tile
+        auto step = [&](auto par_tag, int kt, f32x16 (&cur)[NKT], f32x16 (&nxt)[NKT]) {
+            constexpr int PAR = decltype(par_tag)::value;
+            if (kt + 2 < kt_end) copy_k(kt + 2, PAR);
+            if (kt + 1 < kt_end) copy_v(kt + 1, PAR ^ 1);
+            const int cls_next = cls_of(kt + 1);
+            float mt_next = -INFINITY;
+            if (cls_cur != kEmpty || cls_next != kEmpty) {
+                if (wave_any(mt > m_run + kRescaleLog2)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int t = 0; t < ND; ++t) oacc[t] *= alpha;
+                    m_run = m_new;
+                }
+                mt_next = body(par_tag, cur, nxt, cls_cur == kEmpty);
+            } else {
+                // Both hidden: the next step may run this tile with P = 0, which
+                // needs finite scores.
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) nxt[t] = f32x16{};
+            }
+            if (cls_next == kEdge) {
+                mask_tile(nxt, (kt + 1) * BN);
+                mt_next = tile_max(nxt);
+            }
+            mt = cls_next == kEmpty ? -INFINITY : mt_next;
+            cls_cur = cls_next;
+            if (kt + 1 < kt_end) wait_copies();  // this wave's part of K(kt+2), V(kt+1)
+            __syncthreads();                     // ... and everyone's; stages PAR free again
+        };
+
+        // Prologue: K and V of the first tile, K of the second, and S of the first.
+        f32x16 sa[NKT], sb[NKT];
+        __syncthreads();  // LDS zeroed before the first copy lands
+        copy_k(kt_begin, 0);
+        copy_v(kt_begin, 0);
+        if (kt_begin + 1 < kt_end) copy_k(kt_begin + 1, 1);
+        wait_copies();
+        __syncthreads();
+        if (cls_cur != kEmpty) {
+            s_only(std::integral_constant<int, 0>{}, sa);
+            if (cls_cur == kEdge) mask_tile(sa, kt_begin * BN);
+            mt = tile_max(sa);
+        } else {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) sa[t] = f32x16{};
+        }
+        __syncthreads();  // every wave has read K(kt_begin) before its stage is refilled
+        // Unrolled by two, so the stage parity (and with it every LDS offset) is a
+        // compile-time constant and the score buffers swap roles without copies.
+        for (int kt = kt_begin;;) {
+            step(std::integral_constant<int, 0>{}, kt, sa, sb);
+            if (++kt == kt_end) break;
+            step(std::integral_constant<int, 1>{}, kt, sb, sa);
+            if (++kt == kt_end) break;
+        }
+    } else {
+        constexpr int NPV = BN / 16;  // PV k-steps per tile
+        constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step
+
+        __syncthreads();  // LDS zeroed before the first copy lands
+        copy_tile(kt_begin, 0);
+        land_tile(0);
+        __syncthreads();
+
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int stage = (kt - kt_begin) & 1;
+            if (kt + 1 < kt_end) copy_tile(kt + 1, stage ^ 1);
+
+            const int k0 = kt * BN;
+            const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
+            if (cls != kEmpty) {
+                const uint8_t *Ks = lds + stage * TL::STAGE_BYTES;
+
+                // S^T = K Q^T.
+                f32x16 sacc[NKT];
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) sacc[t] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                    for (int t = 0; t < NKT; ++t) {
+                        const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                            Ks + k_addr[t][s % KP] + (s / KP) * 2 * KP * G * 16);
+                        sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
+                    }
+
+                // Edge tiles only: hidden scores become -inf, so exp2 gives them
+                // exactly 0 below (the scale is never below 1e-30).
+                if (cls == kEdge) {
+#pragma unroll
+                    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+                            if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
+                        }
+                }
+
+                // V^T operands: the reads for PV k-steps s .. s+V_AHEAD-1 are in
+                // flight while the exponentials of step s are computed.
+                const uint32_t v_region = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES;
+                uint32_t v_stage[VT][VH];
+#pragma unroll
+                for (int tb = 0; tb < VT; ++tb)
+#pragma unroll
+                    for (int hb = 0; hb < VH; ++hb) v_stage[tb][hb] = v_region + v_addr[tb][hb];
+                u32x2 vr[NPV][NVR];
+                auto issue_v = [&](auto s_tag) {
+                    constexpr int s = decltype(s_tag)::value;
+                    if constexpr (s < NPV) {
+                        static_for<ND>([&](auto t_tag) {
+                            constexpr int t = decltype(t_tag)::value;
+                            constexpr int toff = (t - t % VT) * 64 * G;
+                            constexpr int lo = (16 * s) / G * 1024 + toff;
+                            constexpr int hi = (16 * s + 8 * (1 - 1 % VH)) / G * 1024 + toff;
+                            vr[s][2 * t] = lds_read_tr16<lo>(v_stage[t % VT][0]);
+                            vr[s][2 * t + 1] = lds_read_tr16<hi>(v_stage[t % VT][1 % VH]);
+                        });
+                    }
+                };
+                static_for<V_AHEAD>(issue_v);
+
+                // Running max; raised (and O, l rescaled) only when it grows by
+                // more than 2^kRescaleLog2.
+                float mx = -INFINITY;
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+                const float mt = half_max(mx) * sl2e;
+                if (wave_any(mt > m_run + kRescaleLog2)) {
+                    const float m_new = fmaxf(m_run, mt);
+                    const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int t = 0; t < ND; ++t) oacc[t] *= alpha;
+                    m_run = m_new;
+                }
+                const float base = (m_run == -INFINITY) ? 0.0f : m_run;
+
+                // P = exp2(s * scale log2e - m), rounded to T; l += sum of the
+                // rounded values; O^T += V^T P^T.
+                static_for<NPV>([&](auto s_tag) {
+                    constexpr int s = decltype(s_tag)::value;
+                    constexpr int o8 = 8 * (s & 1);
+                    u32x4 pb;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e0 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i], sl2e, -base));
+                        const float e1 = exp2_fast(fmaf(sacc[s >> 1][o8 + 2 * i + 1], sl2e, -base));
+                        pb[i] = pack2<T>(e0, e1);
+                        l_run = sum2<T>(pb[i], l_run);
+                    }
+                    lds_wait<(V_AHEAD > 1 && s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
+#pragma unroll
+                    for (int t = 0; t < ND; ++t) {
+                        const u32x4 a = {vr[s][2 * t][0], vr[s][2 * t][1], vr[s][2 * t + 1][0],
+                                         vr[s][2 * t + 1][1]};
+                        oacc[t] = mfma16<T>(a, pb, oacc[t]);
+                    }
+                    issue_v(std::integral_constant<int, s + V_AHEAD>{});
+                });
+            }
+
+            if (kt + 1 < kt_end) land_tile(stage ^ 1);  // this wave's part of the next tile
+            __syncthreads();  // ... and everyone's; the current stage is free again
+        }
     }
 
     // Epilogue: O = O^T / l, written back in BSHD.

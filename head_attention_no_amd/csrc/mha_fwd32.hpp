@@ -51,7 +51,7 @@ void mha_fwd32(Params p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wave = tid >> 6;
     const int c32 = lane & 31;
     const int g = lane >> 5;
 
