@@ -64,13 +64,13 @@ constexpr int kRsrcWord3 = 0x00020000;
 // with the 512-register budget), and the LDS swizzle periods (below).
 template <int D>
 struct Tile16 {
-    static constexpr int BN = D == 32 ? 128 : 8192 / D;  // keys per tile: 128, 128, 64, 32
+    static constexpr int BN = D == 32 ? 128 : D == 256 ? 64 : 8192 / D;  // keys per tile: 128, 128, 64, 64
     static constexpr int NW = D == 256 ? 4 : 8;           // waves per workgroup, 32 query rows each
     static constexpr int WPE = D == 256 ? 1 : 2;          // waves per SIMD
     static constexpr int NKT = BN / 32;           // 32-key sub-tiles of S^T
     static constexpr int ND = D / 32;             // 32-dim sub-tiles of O^T
     static constexpr int G = 512 / D;             // keys per 1 KiB key group
-    static constexpr int TILE_BYTES = BN * D * 2;  // 8 or 16 KiB
+    static constexpr int TILE_BYTES = BN * D * 2;  // 8, 16 or 32 KiB
     static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile, then V tile
     static constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered
     static constexpr int GROUPS = BN / G;         // key groups per tile
@@ -132,6 +132,7 @@ __device__ inline int v_lds_offset(int key, int c)
 template <int OFF>
 __device__ inline u32x2 lds_read_tr16(uint32_t addr)
 {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset field");
     u32x2 r;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
     return r;
@@ -156,6 +157,7 @@ __device__ inline void lds_wait(u32x2 (&r)[N])
 template <int OFF>
 __device__ inline u32x4 lds_read_b128(uint32_t addr)
 {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset field");
     u32x4 r;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
     return r;
@@ -302,17 +304,25 @@ void mha_fwd16(Params p)
         constexpr int NPAIR = 4 * NPV;  // score pairs per lane per tile
         constexpr int KA = TL::PIPE_K_AHEAD, VA = TL::PIPE_V_AHEAD, MD = TL::PIPE_MAX_DELAY;
 
-        // Per-lane LDS read bases; the stage and k-step offsets are immediates.
-        uint32_t kb[NKT][KP];
+        // Per-lane LDS read bases; the k-step offsets are immediates, and so
+        // is the stage offset unless the 16-bit immediate cannot reach the
+        // second stage (64 KiB stages at D = 256): then each stage has its
+        // own bases.
+        constexpr int NB = 2 * TL::STAGE_BYTES > 65536 ? 2 : 1;
+        constexpr int IMM_STAGE = NB == 1 ? TL::STAGE_BYTES : 0;
+        uint32_t kb[NB][NKT][KP];
+        uint32_t vb[NB][VT][VH];
 #pragma unroll
-        for (int t = 0; t < NKT; ++t)
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-            for (int q = 0; q < KP; ++q) kb[t][q] = lds_base + k_addr[t][q];
-        uint32_t vb[VT][VH];
+            for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int tb = 0; tb < VT; ++tb)
+                for (int q = 0; q < KP; ++q) kb[nb][t][q] = lds_base + nb * TL::STAGE_BYTES + k_addr[t][q];
 #pragma unroll
-            for (int hb = 0; hb < VH; ++hb) vb[tb][hb] = lds_base + v_addr[tb][hb];
+            for (int tb = 0; tb < VT; ++tb)
+#pragma unroll
+                for (int hb = 0; hb < VH; ++hb) vb[nb][tb][hb] = lds_base + nb * TL::STAGE_BYTES + v_addr[tb][hb];
+        }
 
         // K and V of a tile are copied one step apart: K(kt) goes to stage
         // (kt - kt_begin) & 1 one step before V(kt) goes to the same stage.
@@ -352,15 +362,15 @@ void mha_fwd16(Params p)
         auto k_read = [&](auto par_tag, auto m_tag) {
             constexpr int PAR = decltype(par_tag)::value, m = decltype(m_tag)::value;
             constexpr int s = m / NKT, t = m % NKT;
-            return lds_read_b128<PAR * TL::STAGE_BYTES + (s / KP) * 2 * KP * G * 16>(kb[t][s % KP]);
+            return lds_read_b128<PAR * IMM_STAGE + (s / KP) * 2 * KP * G * 16>(kb[PAR % NB][t][s % KP]);
         };
         // The two transposing reads for PV MFMA j (k-step j / ND, 32-dim sub-tile j % ND) from stage PAR.
         auto v_read = [&](auto par_tag, auto j_tag, u32x2 (&dst)[2]) {
             constexpr int PAR = decltype(par_tag)::value, j = decltype(j_tag)::value;
             constexpr int s = j / ND, t = j % ND;
-            constexpr int base = PAR * TL::STAGE_BYTES + TL::TILE_BYTES + (t - t % VT) * 64 * G;
-            dst[0] = lds_read_tr16<base + (16 * s) / G * 1024>(vb[t % VT][0]);
-            dst[1] = lds_read_tr16<base + (16 * s + 8 * (1 - 1 % VH)) / G * 1024>(vb[t % VT][1 % VH]);
+            constexpr int base = PAR * IMM_STAGE + TL::TILE_BYTES + (t - t % VT) * 64 * G;
+            dst[0] = lds_read_tr16<base + (16 * s) / G * 1024>(vb[PAR % NB][t % VT][0]);
+            dst[1] = lds_read_tr16<base + (16 * s + 8 * (1 - 1 % VH)) / G * 1024>(vb[PAR % NB][t % VT][1 % VH]);
         };
         // S = K Q^T of the first tile, not interleaved.
         auto s_only = [&](auto par_tag, f32x16 (&sc)[NKT]) {
