@@ -2,7 +2,8 @@
 //
 // Host side: argument validation (before any HIP call), the gfx950 device
 // check, the choice of kernel instance (dtype x head dim x mask kind) and the
-// launch on the caller's stream.
+// launch on the caller's stream. The attention kernel instances are compiled
+// in mha_launch.hip; this unit holds the top-K kernel.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -14,6 +15,7 @@
 #include "fa355.h"
 #include "mha_fwd16.hpp"
 #include "mha_fwd32.hpp"
+#include "mha_launch.hpp"
 #include "topk.hpp"
 
 namespace {
@@ -106,36 +108,14 @@ int check_device()
     return state == 1 ? FA355_OK : FA355_ERR_DEVICE;
 }
 
-template <typename T, int D, int MASK>
-hipError_t launch_one(const Params &p, int grid, hipStream_t stream)
-{
-    void *args[] = {const_cast<Params *>(&p)};
-    if constexpr (std::is_same_v<T, float>)
-        return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd32<D, MASK>),
-                               dim3(grid), dim3(fa355::kThreads32), args, 0, stream);
-    else
-        return hipLaunchKernel(reinterpret_cast<const void *>(&fa355::mha_fwd16<T, D, MASK>),
-                               dim3(grid), dim3(64 * fa355::Tile16<D>::NW), args, 0, stream);
-}
-
-template <typename T, int D>
-hipError_t launch_mask(const Params &p, int mask, int grid, hipStream_t stream)
-{
-    switch (mask) {
-    case FA355_MASK_NONE: return launch_one<T, D, fa355::kMaskNone>(p, grid, stream);
-    case FA355_MASK_CAUSAL: return launch_one<T, D, fa355::kMaskCausal>(p, grid, stream);
-    default: return launch_one<T, D, fa355::kMaskWindow>(p, grid, stream);
-    }
-}
-
 template <typename T>
 hipError_t launch_dim(const Params &p, int D, int mask, int grid, hipStream_t stream)
 {
     switch (D) {
-    case 32: return launch_mask<T, 32>(p, mask, grid, stream);
-    case 64: return launch_mask<T, 64>(p, mask, grid, stream);
-    case 128: return launch_mask<T, 128>(p, mask, grid, stream);
-    default: return launch_mask<T, 256>(p, mask, grid, stream);
+    case 32: return fa355::launch_mha<T, 32>(p, mask, grid, stream);
+    case 64: return fa355::launch_mha<T, 64>(p, mask, grid, stream);
+    case 128: return fa355::launch_mha<T, 128>(p, mask, grid, stream);
+    default: return fa355::launch_mha<T, 256>(p, mask, grid, stream);
     }
 }
 
