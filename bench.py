@@ -290,7 +290,8 @@ def yardsticks(w, steps: int, warmup: int):
 
 
 # Sources of the attention path (the top-K kernel is not part of it).
-ATTENTION_SOURCES = ("fa355.hip", "mha_common.hpp", "mha_fwd16.hpp", "mha_fwd32.hpp")
+ATTENTION_SOURCES = ("fa355.hip", "mha_common.hpp", "mha_fwd16.hpp", "mha_fwd32.hpp", "mha_launch.hip",
+                     "mha_launch.hpp")
 
 
 def kernel_sources_hash() -> str:

@@ -109,13 +109,13 @@ int check_device()
 }
 
 template <typename T>
-hipError_t launch_dim(const Params &p, int D, int mask, int grid, hipStream_t stream)
+hipError_t launch_dim(const Params &p, int D, int mask, hipStream_t stream)
 {
     switch (D) {
-    case 32: return fa355::launch_mha<T, 32>(p, mask, grid, stream);
-    case 64: return fa355::launch_mha<T, 64>(p, mask, grid, stream);
-    case 128: return fa355::launch_mha<T, 128>(p, mask, grid, stream);
-    default: return fa355::launch_mha<T, 256>(p, mask, grid, stream);
+    case 32: return fa355::launch_mha<T, 32>(p, mask, stream);
+    case 64: return fa355::launch_mha<T, 64>(p, mask, stream);
+    case 128: return fa355::launch_mha<T, 128>(p, mask, stream);
+    default: return fa355::launch_mha<T, 256>(p, mask, stream);
     }
 }
 
@@ -173,12 +173,13 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
 
     const int grid = p.n_qtiles * B * (H / p.hp);
+    p.n_items = grid;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (dtype) {
-    case FA355_BF16: err = launch_dim<__bf16>(p, D, mask_kind, grid, s); break;
-    case FA355_F16: err = launch_dim<_Float16>(p, D, mask_kind, grid, s); break;
-    default: err = launch_dim<float>(p, D, mask_kind, grid, s); break;
+    case FA355_BF16: err = launch_dim<__bf16>(p, D, mask_kind, s); break;
+    case FA355_F16: err = launch_dim<_Float16>(p, D, mask_kind, s); break;
+    default: err = launch_dim<float>(p, D, mask_kind, s); break;
     }
     return err == hipSuccess ? FA355_OK : FA355_ERR_LAUNCH;
 }

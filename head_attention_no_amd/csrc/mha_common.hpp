@@ -38,6 +38,7 @@ struct Params {
     int hp;        // query heads per workgroup: a divisor of rep, so they share one K/V head
     int wph;       // waves per query head: the workgroup's waves / hp
     int n_qtiles;  // ceil(S / query rows per head per workgroup)
+    int n_items;   // work items: n_qtiles * B * H / hp (the grid may be smaller)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|

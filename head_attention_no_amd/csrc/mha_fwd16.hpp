@@ -86,6 +86,10 @@ struct Tile16 {
     // the power cap, where the extra S MFMAs of each wave's last tile cost
     // more than the overlap gains).
     static constexpr bool PIPELINE = D == 64 || D == 256;
+    // The plain loop can walk several work items per workgroup (prefetching
+    // the next item's Q rows and first K/V tile); the launcher uses that at
+    // D = 128 only.
+    static constexpr bool WALK = D == 128;
     static constexpr int PIPE_K_AHEAD = 3;    // K operand reads issued this many MFMAs ahead
     static constexpr int PIPE_V_AHEAD = 4;    // V operand pairs issued this many MFMAs ahead
     static constexpr int PIPE_MAX_DELAY = 3;  // MFMAs between the last S MFMA and its max
@@ -180,6 +184,32 @@ __device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds_dst,
 // Wait for this wave's outstanding global -> LDS copies (vmcnt = 0).
 __device__ inline void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One work item (a query tile of hp heads sharing a K/V head) as one wave
+// of the workgroup sees it.
+struct WaveItem {
+    int b, kvh, h;           // batch, K/V head, this wave's query head
+    int q0, wrow0, row;      // first row of the tile, of this wave, of this lane
+    int kt_begin, kt_end;    // key tiles the workgroup visits
+    int64_t kv_head0;        // byte offset of K/V[b, 0, kvh, 0]
+};
+
+template <int D, int MASK, int BN>
+__device__ inline WaveItem wave_item(const Params &p, int item, int wave, int c32)
+{
+    const TileCoord tc = block_coord(item, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
+    const int rows = 32 * p.wph;  // query rows per head in the workgroup
+    WaveItem it;
+    it.b = tc.b;
+    it.kvh = tc.h / p.rep;
+    it.h = tc.h + wave / p.wph;
+    it.q0 = tc.qt * rows;
+    it.wrow0 = it.q0 + (wave % p.wph) * 32;
+    it.row = it.wrow0 + c32;
+    it.kv_head0 = ((int64_t)it.b * p.S * p.Hkv + it.kvh) * D * 2;
+    key_tile_range<MASK, BN>(it.q0, rows, p.S, p.window, it.kt_begin, it.kt_end);
+    return it;
+}
+
 // Tile16<D>::NW waves per workgroup, 32 query rows each.
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(64 * Tile16<D>::NW)
@@ -196,7 +226,11 @@ void mha_fwd16(Params p)
     constexpr int ND = TL::ND;
     constexpr int G = TL::G;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::LDS_BYTES];
+    // K/V stages, then (plain loop only) each wave's 32 Q rows of the next
+    // work item: D / 16 blocks of 1 KiB, lane l's 16 bytes of k-step s at
+    // block s, byte 16 l.
+    constexpr int Q_LDS_BYTES = TL::WALK ? NW * D * 64 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[TL::LDS_BYTES + Q_LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -204,22 +238,15 @@ void mha_fwd16(Params p)
     const int c32 = lane & 31;
     const int g = lane >> 5;
 
-    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
-    const int b = tc.b, kvh = tc.h / p.rep;
-    const int h = tc.h + wave / p.wph;  // this wave's query head
-    const int rows = 32 * p.wph;        // query rows per head in this workgroup
+    const WaveItem it0 = wave_item<D, MASK, BN>(p, blockIdx.x, wave, c32);
     const int S = p.S, W = p.window;
-    const int q0 = tc.qt * rows;
-    const int wrow0 = q0 + (wave % p.wph) * 32;
-    const int row = wrow0 + c32;  // this lane's query row
+    const int wrow0 = it0.wrow0, row = it0.row;
 
-    const T *__restrict__ Q = static_cast<const T *>(p.q);
     T *__restrict__ O = static_cast<T *>(p.out);
     const int64_t q_row_stride = (int64_t)p.H * D;
     const uint32_t kv_stride = (uint32_t)p.Hkv * D * 2;  // bytes between key rows
-    const int64_t kv_head0 = ((int64_t)b * S * p.Hkv + kvh) * D * 2;
-    const uint8_t *Kbh = static_cast<const uint8_t *>(p.k) + kv_head0;
-    const uint8_t *Vbh = static_cast<const uint8_t *>(p.v) + kv_head0;
+    const uint8_t *Kbh = static_cast<const uint8_t *>(p.k) + it0.kv_head0;
+    const uint8_t *Vbh = static_cast<const uint8_t *>(p.v) + it0.kv_head0;
 
     // LDS starts zeroed, so a slot no copy writes still holds finite data.
     for (int i = tid; i < TL::LDS_BYTES / 16; i += NTHREADS)
@@ -227,12 +254,14 @@ void mha_fwd16(Params p)
 
     // Q fragments: qf[s] = Q[row][16s + 8g .. +7]. Rows past the end of the
     // sequence read the last row (their results are never stored).
-    u32x4 qf[D / 16];
-    {
-        const T *qrow = Q + ((int64_t)b * S + min(row, S - 1)) * q_row_stride + (int64_t)h * D;
+    auto load_q = [&](const WaveItem &it, u32x4 (&dst)[D / 16]) {
+        const T *qrow = static_cast<const T *>(p.q) + ((int64_t)it.b * S + min(it.row, S - 1)) * q_row_stride +
+                        (int64_t)it.h * D;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) qf[s] = ldg16(qrow + 16 * s + 8 * g) ^ p.q_sign;
-    }
+        for (int s = 0; s < D / 16; ++s) dst[s] = ldg16(qrow + 16 * s + 8 * g) ^ p.q_sign;
+    };
+    u32x4 qf[D / 16];
+    load_q(it0, qf);
 
     // Copy offsets: wave w copies key groups w, w+NW, ... of K and of V;
     // lane l fills slot l of the group's 1 KiB block.
@@ -252,8 +281,8 @@ void mha_fwd16(Params p)
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base) + (int64_t)k0 * kv_stride,
                                                  0, nrec, kRsrcWord3);
     };
-    auto copy_tile = [&](int kt, int stage) {
-        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(Kbh, kt), rv = tile_rsrc(Vbh, kt);
+    auto copy_tile = [&](const uint8_t *kbase, const uint8_t *vbase, int kt, int stage) {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, kt), rv = tile_rsrc(vbase, kt);
         uint8_t *kdst = lds + stage * TL::STAGE_BYTES;
         uint8_t *vdst = kdst + TL::TILE_BYTES;
 #pragma unroll
@@ -293,8 +322,23 @@ void mha_fwd16(Params p)
     float l_run = 0.0f;       // this lane's share of the running sum
     const float sl2e = p.scale_log2;
 
-    int kt_begin, kt_end;
-    key_tile_range<MASK, BN>(q0, rows, S, W, kt_begin, kt_end);
+    const int kt_begin = it0.kt_begin, kt_end = it0.kt_end;
+
+    // Epilogue: O = O^T / l, written back in BSHD.
+    auto store_out = [&](const WaveItem &it) {
+        const float inv = 1.0f / half_sum(l_run);
+        if (it.row < S) {
+            T *orow = O + ((int64_t)it.b * S + it.row) * q_row_stride + (int64_t)it.h * D;
+#pragma unroll
+            for (int t = 0; t < ND; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 w = {pack2<T>(oacc[t][4 * i] * inv, oacc[t][4 * i + 1] * inv),
+                                     pack2<T>(oacc[t][4 * i + 2] * inv, oacc[t][4 * i + 3] * inv)};
+                    *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * i + 4 * g) = w;
+                }
+        }
+    };
 
     if constexpr (TL::PIPELINE) {
         constexpr int NPV = BN / 16;    // PV k-steps per tile
@@ -559,45 +603,106 @@ void mha_fwd16(Params p)
             step(std::integral_constant<int, 1>{}, kt, sb, sa);
             if (++kt == kt_end) break;
         }
+        store_out(it0);
     } else {
         constexpr int NPV = BN / 16;  // PV k-steps per tile
         constexpr int NVR = 2 * ND;   // transposing V reads per PV k-step
 
+        // Persistent walk: with fewer workgroups than work items (one per
+        // resident slot, a multiple of 8), workgroup w takes in round r the
+        // item of slot r C + (r even ? w / 8 : C - 1 - w / 8) on its own XCD
+        // (item = 8 slot + w % 8, C = grid / 8), so the longest-first order
+        // is walked forward and back (round lengths balance) and every item
+        // keeps the XCD the item order intends. During an item's last tile
+        // the next item's first K/V tile and Q fragments are already on the
+        // way.
+        const int n_slot = gridDim.x / 8, xcd = blockIdx.x % 8, slot0 = blockIdx.x / 8;
+        const bool walk = TL::WALK && gridDim.x % 8 == 0 && (int)gridDim.x < p.n_items;
+        auto item_index = [&](int r) {
+            return (r * n_slot + ((r & 1) ? n_slot - 1 - slot0 : slot0)) * 8 + xcd;
+        };
+        // This wave's Q rows of item `it` go global -> LDS (the wave reads them
+        // back itself, after its own copies have landed). The resource starts
+        // at the wave's first row (clamped to the sequence) and ends at its
+        // last row in the sequence; rows past the end read row S - 1.
+        uint8_t *const q_lds = lds + TL::LDS_BYTES + (TL::WALK ? wave * D * 64 : 0);
+        auto copy_q = [&](const WaveItem &it) {
+            const int r0 = min(it.wrow0, S - 1), r1 = min(it.wrow0 + 31, S - 1);
+            const uint32_t row_bytes = (uint32_t)q_row_stride * 2;
+            const uint8_t *base = static_cast<const uint8_t *>(p.q) +
+                                  (((int64_t)it.b * S + r0) * q_row_stride + (int64_t)it.h * D) * 2;
+            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(base), 0, (int)((r1 - r0) * row_bytes + D * 2), kRsrcWord3);
+            const uint32_t voff = (uint32_t)(min(it.row, S - 1) - r0) * row_bytes + 16 * g;
+            if constexpr (TL::WALK) {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) lds_copy16(rq, q_lds + s * 1024, voff + 32 * s);
+            }
+        };
+        auto kbase = [&](const WaveItem &it) { return static_cast<const uint8_t *>(p.k) + it.kv_head0; };
+        auto vbase = [&](const WaveItem &it) { return static_cast<const uint8_t *>(p.v) + it.kv_head0; };
+
+        WaveItem cur = it0;
+        int rnd = 0, kt = kt_begin, stage = 0;
         __syncthreads();  // LDS zeroed before the first copy lands
-        copy_tile(kt_begin, 0);
+        copy_tile(Kbh, Vbh, kt, 0);
         land_tile(0);
         __syncthreads();
 
-        for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int stage = (kt - kt_begin) & 1;
-            if (kt + 1 < kt_end) copy_tile(kt + 1, stage ^ 1);
+        for (;;) {
+            const bool last = kt + 1 == cur.kt_end;
+            const int next_idx = walk && last ? item_index(rnd + 1) : p.n_items;
+            const bool more = next_idx < p.n_items;
+            WaveItem nxt = cur;
+            if (!last) {
+                copy_tile(kbase(cur), vbase(cur), kt + 1, stage ^ 1);
+            } else if (more) {
+                nxt = wave_item<D, MASK, BN>(p, next_idx, wave, c32);
+                copy_tile(kbase(nxt), vbase(nxt), nxt.kt_begin, stage ^ 1);
+                copy_q(nxt);
+            }
+            const int wrow0 = cur.wrow0, row = cur.row;
 
             const int k0 = kt * BN;
             const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
             if (cls != kEmpty) {
-                const uint8_t *Ks = lds + stage * TL::STAGE_BYTES;
-
-                // S^T = K Q^T.
+                // S^T = K Q^T: MFMA m takes k-step m / NKT of sub-tile m % NKT; its
+                // K operand is read KA MFMAs ahead (explicit reads and counted
+                // waits, so the schedule does not depend on the compiler's).
+                constexpr int NSM = D / 16 * NKT;
+                constexpr int KA = NSM < 4 ? NSM : 4;
+                const uint32_t k_stage = lds_base + stage * TL::STAGE_BYTES;
+                uint32_t kb[NKT][KP];
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int q = 0; q < KP; ++q) kb[t][q] = k_stage + k_addr[t][q];
+                auto k_read = [&](auto m_tag) {
+                    constexpr int m = decltype(m_tag)::value, s = m / NKT, t = m % NKT;
+                    return lds_read_b128<(s / KP) * 2 * KP * G * 16>(kb[t][s % KP]);
+                };
                 f32x16 sacc[NKT];
-#pragma unroll
-                for (int t = 0; t < NKT; ++t) sacc[t] = f32x16{};
-#pragma unroll
-                for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-                    for (int t = 0; t < NKT; ++t) {
-                        const u32x4 a = *reinterpret_cast<const u32x4 *>(
-                            Ks + k_addr[t][s % KP] + (s / KP) * 2 * KP * G * 16);
-                        sacc[t] = mfma16<T>(a, qf[s], sacc[t]);
-                    }
+                u32x4 kr[NSM];
+                static_for<KA>([&](auto m_tag) { kr[m_tag] = k_read(m_tag); });
+                static_for<NSM>([&](auto m_tag) {
+                    constexpr int m = decltype(m_tag)::value;
+                    lds_wait4<(m + KA <= NSM ? KA : NSM - m) - 1>(kr[m]);
+                    sacc[m % NKT] = mfma16<T>(kr[m], qf[m / NKT], m < NKT ? f32x16{} : sacc[m % NKT]);
+                    if constexpr (m + KA < NSM) kr[m + KA] = k_read(std::integral_constant<int, m + KA>{});
+                });
 
                 // Edge tiles only: hidden scores become -inf, so exp2 gives them
                 // exactly 0 below (the scale is never below 1e-30).
                 if (cls == kEdge) {
+                    // The lane's first key, opaque to the optimiser: otherwise it
+                    // keeps all 32 lane offsets in registers across the loop.
+                    int key0 = k0 + 4 * g;
+                    asm volatile("" : "+v"(key0));
 #pragma unroll
                     for (int t = 0; t < NKT; ++t)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+                            const int key = key0 + 32 * t + 8 * (r >> 2) + (r & 3);
                             if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
                         }
                 }
@@ -668,24 +773,30 @@ void mha_fwd16(Params p)
                 });
             }
 
-            if (kt + 1 < kt_end) land_tile(stage ^ 1);  // this wave's part of the next tile
+            if (!last || more) land_tile(stage ^ 1);  // this wave's part of the next tile (and its Q rows)
+            if (last) {
+                store_out(cur);
+                if (!more) break;
+                m_run = -INFINITY;
+                l_run = 0.0f;
+#pragma unroll
+                for (int t = 0; t < ND; ++t) oacc[t] = f32x16{};
+                if constexpr (TL::WALK) {
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s)
+                        qf[s] = *reinterpret_cast<const u32x4 *>(q_lds + s * 1024 + 16 * lane) ^ p.q_sign;
+                }
+                cur = nxt;
+                kt = cur.kt_begin;
+                ++rnd;
+            } else {
+                ++kt;
+            }
+            stage ^= 1;
             __syncthreads();  // ... and everyone's; the current stage is free again
         }
     }
 
-    // Epilogue: O = O^T / l, written back in BSHD.
-    const float inv = 1.0f / half_sum(l_run);
-    if (row < S) {
-        T *orow = O + ((int64_t)b * S + row) * q_row_stride + (int64_t)h * D;
-#pragma unroll
-        for (int t = 0; t < ND; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x2 w = {pack2<T>(oacc[t][4 * i] * inv, oacc[t][4 * i + 1] * inv),
-                                 pack2<T>(oacc[t][4 * i + 2] * inv, oacc[t][4 * i + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * i + 4 * g) = w;
-            }
-    }
 }
 
 }  // namespace fa355

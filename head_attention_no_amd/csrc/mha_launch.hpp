@@ -12,8 +12,9 @@
 namespace fa355 {
 
 // Launches the kernel for element type T (__bf16, _Float16 or float), head
-// dim D and mask kind `mask` (MaskKind) on `grid` workgroups of `stream`.
+// dim D and mask kind `mask` (MaskKind) on `stream`, for the p.n_items work
+// items (one workgroup each, or fewer workgroups that each walk several).
 template <typename T, int D>
-hipError_t launch_mha(const Params &p, int mask, int grid, hipStream_t stream);
+hipError_t launch_mha(const Params &p, int mask, hipStream_t stream);
 
 }  // namespace fa355

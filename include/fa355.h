@@ -116,11 +116,15 @@ const char *fa355_version(void);
  * query rows of heads_per_wg consecutive query heads, which share one K/V
  * head (heads_per_wg is the largest of 8, 4, 2, 1 that divides H / Hkv and
  * fits the kernel's waves), against key tiles of block_n keys. Given the
- * call's shape, reports the number of workgroups and, for each of the first
- * `n` workgroup indices, what it computes: tiles[3*w + 0] = query tile (rows
+ * call's shape, reports the number of such work items (num_workgroups) and,
+ * for each of the first `n` item indices, in the longest-first order the
+ * library launches them, what it computes: tiles[3*w + 0] = query tile (rows
  * tile*block_m ... tile*block_m + block_m - 1), tiles[3*w + 1] = b,
- * tiles[3*w + 2] = first head h (heads h ... h + heads_per_wg - 1). Any
- * output pointer may be NULL; `tiles` NULL queries only the sizes.
+ * tiles[3*w + 2] = first head h (heads h ... h + heads_per_wg - 1). The
+ * library launches one workgroup per item, or, for short items at head dim
+ * 128, as many workgroups as the device holds at once (a multiple of 8),
+ * each taking several items in a fixed order. Any output pointer may be
+ * NULL; `tiles` NULL queries only the sizes.
  * Returns FA355_OK or FA355_ERR_INVALID_ARG / FA355_ERR_UNSUPPORTED under
  * the same rules as mha_no_cache.
  */

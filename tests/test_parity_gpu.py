@@ -260,3 +260,30 @@ def test_rows_past_the_end_are_never_used(dt, D, mask):
     out = fa.attention(q.to(DEV), guarded(k), guarded(v), 1.0 / math.sqrt(D), mask)
     torch.cuda.synchronize()
     check(out.cpu(), oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask), dt, f"tail {dt} {mask}")
+
+
+WALK = [
+    # B, S, H, Hkv, D, dtype, mask, window: more work items than the GPU holds
+    # workgroups. At D = 128 with short items each workgroup walks several
+    # items, the last round only partly filled; the D = 32 case launches one
+    # workgroup per item.
+    (2, 1100, 32, 8, 128, "bf16", "causal", -1),
+    (1, 1100, 64, 8, 128, "bf16", "sliding_window", 200),
+    (2, 1037, 32, 8, 128, "f16", "none", -1),
+    (1, 600, 128, 128, 32, "bf16", "causal", -1),
+]
+
+
+@pytest.mark.parametrize("case", WALK, ids=lambda c: "B{}_S{}_H{}kv{}_D{}_{}_{}_W{}".format(*c))
+def test_walk_over_many_items_whole_output(case):
+    B, S, H, Hkv, D, dt, mask, window = case
+    note(f"walk case {case}")
+    items = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt])["num_workgroups"]
+    assert items > torch.cuda.get_device_properties(0).multi_processor_count
+    q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + H + D)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    fa.attention(*_dev(q, k, v), 1.0 / math.sqrt(D), mask, window, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert not torch.isnan(got.float()).any(), "some output element was never written"
+    check(got, oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask, window), dt, str(case))
