@@ -117,6 +117,19 @@ __device__ inline bool visible(int row, int key, int S, int W)
     return true;
 }
 
+// The keys query `row` may see among key0 .. key0 + n - 1 (the set visible()
+// accepts), as offsets from key0: off in [lo, hi]. Without a window lo is
+// not needed (the set starts at key 0); with one, an empty set comes back
+// as lo = hi = n, which the test (unsigned)(off - lo) <= hi - lo rejects
+// for every off in 0 .. n-1.
+template <int MASK>
+__device__ inline void visible_range(int row, int key0, int S, int W, int n, int &lo, int &hi)
+{
+    hi = (MASK == kMaskNone ? S - 1 : min(row, S - 1)) - key0;
+    lo = MASK == kMaskWindow ? row - W + 1 - key0 : 0;
+    if (MASK == kMaskWindow && hi < lo) lo = hi = n;
+}
+
 // Key-tile range [begin, end) a workgroup whose rows (per head) are
 // q0 .. q0+rows-1 must visit.
 template <int MASK, int BN>

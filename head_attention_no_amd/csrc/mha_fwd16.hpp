@@ -385,13 +385,19 @@ void mha_fwd16(Params p)
         auto cls_of = [&](int kt) {
             return kt < kt_end ? classify<MASK>(wrow0, kt * BN, kt * BN + BN - 1, S, W) : (int)kEmpty;
         };
+        // Element (t, r) holds key k0 + 4g + 32t + 8(r/4) + r%4 (see the
+        // plain loop's edge mask).
         auto mask_tile = [&](f32x16 (&sc)[NKT], int k0) {
+            int lo, hi;
+            visible_range<MASK>(row, k0 + 4 * g, S, W, BN, lo, hi);
+            const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (!visible<MASK>(row, key, S, W)) sc[t][r] = -INFINITY;
+                    const int off = 32 * t + 8 * (r >> 2) + (r & 3);
+                    const bool vis = MASK == kMaskWindow ? (uint32_t)(off - lo) <= span : off <= hi;
+                    if (!vis) sc[t][r] = -INFINITY;
                 }
         };
         auto tile_max = [&](f32x16 (&sc)[NKT]) {
@@ -693,17 +699,21 @@ void mha_fwd16(Params p)
 
                 // Edge tiles only: hidden scores become -inf, so exp2 gives them
                 // exactly 0 below (the scale is never below 1e-30).
+                // Element (t, r) holds key k0 + 4g + off, with the compile-time
+                // offset off = 32t + 8(r/4) + r%4. The lane's visible offsets form
+                // one range [lo, hi], so an element costs a compare and a select
+                // (the window test is one unsigned compare against the span).
                 if (cls == kEdge) {
-                    // The lane's first key, opaque to the optimiser: otherwise it
-                    // keeps all 32 lane offsets in registers across the loop.
-                    int key0 = k0 + 4 * g;
-                    asm volatile("" : "+v"(key0));
+                    int lo, hi;
+                    visible_range<MASK>(row, k0 + 4 * g, S, W, BN, lo, hi);
+                    const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
                     for (int t = 0; t < NKT; ++t)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int key = key0 + 32 * t + 8 * (r >> 2) + (r & 3);
-                            if (!visible<MASK>(row, key, S, W)) sacc[t][r] = -INFINITY;
+                            const int off = 32 * t + 8 * (r >> 2) + (r & 3);
+                            const bool vis = MASK == kMaskWindow ? (uint32_t)(off - lo) <= span : off <= hi;
+                            if (!vis) sacc[t][r] = -INFINITY;
                         }
                 }
 
