@@ -54,7 +54,7 @@ def load(path: str = LIB_PATH):
     lib.fa355_version.argtypes = []
     lib.fa355_version.restype = ctypes.c_char_p
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.fa355_plan.argtypes = [i, i, i, i, i, i, ip, ip, ip, ip, ip, i]
+    lib.fa355_plan.argtypes = [i, i, i, i, i, i, i, i, ip, ip, ip, ip, ip, ip, i]
     lib.fa355_plan.restype = i
     lib.fa355_topk.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.fa355_topk.restype = i
@@ -78,20 +78,24 @@ def version() -> str:
     return load().fa355_version().decode()
 
 
-def plan(B: int, S: int, H: int, Hkv: int, D: int, dtype: int, with_tiles: bool = False):
+def plan(B: int, S: int, H: int, Hkv: int, D: int, dtype: int, mask="none", window: int = -1,
+         with_tiles: bool = False):
     """Work decomposition: dict(num_workgroups, block_m, block_n,
-    heads_per_workgroup[, tiles]); each tile is (query tile, b, first head)."""
+    heads_per_workgroup, walk[, tiles]); each tile is (query tile, b, first
+    head), in item order."""
     lib = load()
-    nwg, bm, bn, hp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, ctypes.byref(nwg), ctypes.byref(bm),
-                        ctypes.byref(bn), ctypes.byref(hp), None, 0)
+    mk = MASKS[mask] if isinstance(mask, str) else int(mask)
+    nwg, bm, bn, hp, walk = (ctypes.c_int() for _ in range(5))
+    rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, mk, window, ctypes.byref(nwg), ctypes.byref(bm),
+                        ctypes.byref(bn), ctypes.byref(hp), ctypes.byref(walk), None, 0)
     if rc != OK:
         raise FA355Error(rc, "fa355_plan")
     res = {"num_workgroups": nwg.value, "block_m": bm.value, "block_n": bn.value,
-           "heads_per_workgroup": hp.value}
+           "heads_per_workgroup": hp.value, "walk": walk.value}
     if with_tiles:
         buf = (ctypes.c_int * (3 * nwg.value))()
-        rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, None, None, None, None, buf, nwg.value)
+        rc = lib.fa355_plan(B, S, H, Hkv, D, dtype, mk, window, None, None, None, None, None, buf,
+                            nwg.value)
         if rc != OK:
             raise FA355Error(rc, "fa355_plan")
         res["tiles"] = [tuple(buf[3 * w:3 * w + 3]) for w in range(nwg.value)]

@@ -90,6 +90,31 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     return FA355_OK;
 }
 
+// Mask kind and window as mha_no_cache checks them.
+int check_mask(int mask_kind, int window)
+{
+    if (mask_kind != FA355_MASK_NONE && mask_kind != FA355_MASK_CAUSAL &&
+        mask_kind != FA355_MASK_SLIDING_WINDOW)
+        return FA355_ERR_INVALID_ARG;
+    if (mask_kind == FA355_MASK_SLIDING_WINDOW && window < 1) return FA355_ERR_INVALID_ARG;
+    return FA355_OK;
+}
+
+// Window width the kernels use: clamped to S (a window >= S is causal).
+int clamped_window(int mask_kind, int window, int S)
+{
+    return mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
+}
+
+// Whether the call walks its work items (walk order; see fa355::walks).
+int call_walks(int dtype, int D, int rep, int mask_kind, int S, int window_clamped)
+{
+    return fa355::walks(dtype != FA355_F32, D, mask_kind, S, window_clamped, block_m(dtype, D, rep),
+                        block_n(dtype, D))
+               ? 1
+               : 0;
+}
+
 // Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
@@ -129,10 +154,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     if (!out || !q || !k || !v) return FA355_ERR_INVALID_ARG;
     int rc = check_shape(B, S, H, Hkv, D, dtype);
     if (rc == FA355_ERR_INVALID_ARG) return rc;
-    if (mask_kind != FA355_MASK_NONE && mask_kind != FA355_MASK_CAUSAL &&
-        mask_kind != FA355_MASK_SLIDING_WINDOW)
-        return FA355_ERR_INVALID_ARG;
-    if (mask_kind == FA355_MASK_SLIDING_WINDOW && window < 1) return FA355_ERR_INVALID_ARG;
+    if (check_mask(mask_kind, window) != FA355_OK) return FA355_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA355_ERR_INVALID_ARG;
     const int64_t es = elem_size(dtype);
     const int64_t q_bytes = (int64_t)B * S * H * D * es;
@@ -162,7 +184,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.hp = heads_per_wg(dtype, D, p.rep);
     p.wph = waves_per_wg(dtype, D) / p.hp;
     p.n_qtiles = (S + 32 * p.wph - 1) / (32 * p.wph);
-    p.window = mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
+    p.window = clamped_window(mask_kind, window, S);
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
     // A scale below 1e-30 in magnitude is taken as 1e-30: for any fp32 score
@@ -174,6 +196,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
 
     const int grid = p.n_qtiles * B * (H / p.hp);
     p.n_items = grid;
+    p.walk = call_walks(dtype, D, p.rep, mask_kind, S, p.window);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (dtype) {
@@ -221,23 +244,27 @@ extern "C" const char *fa355_strerror(int status)
 
 extern "C" const char *fa355_version(void) { return "fa355 0.1.0 gfx950"; }
 
-extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups,
-                          int *block_m_out, int *block_n_out, int *heads_per_wg_out, int *tiles,
-                          int n)
+extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int mask_kind, int window,
+                          int *num_workgroups, int *block_m_out, int *block_n_out,
+                          int *heads_per_wg_out, int *walk_out, int *tiles, int n)
 {
-    const int rc = check_shape(B, S, H, Hkv, D, dtype);
+    int rc = check_shape(B, S, H, Hkv, D, dtype);
+    if (rc == FA355_ERR_INVALID_ARG) return rc;
+    if (check_mask(mask_kind, window) != FA355_OK) return FA355_ERR_INVALID_ARG;
     if (rc != FA355_OK) return rc;
     const int rep = H / Hkv, hp = heads_per_wg(dtype, D, rep), bm = block_m(dtype, D, rep);
     const int n_qtiles = (S + bm - 1) / bm;
     const int grid = n_qtiles * B * (H / hp);
+    const int walk = call_walks(dtype, D, rep, mask_kind, S, clamped_window(mask_kind, window, S));
     if (num_workgroups) *num_workgroups = grid;
     if (block_m_out) *block_m_out = bm;
     if (block_n_out) *block_n_out = block_n(dtype, D);
     if (heads_per_wg_out) *heads_per_wg_out = hp;
+    if (walk_out) *walk_out = walk;
     if (tiles) {
         if (n < 0) return FA355_ERR_INVALID_ARG;
         for (int w = 0; w < n && w < grid; ++w) {
-            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv, hp);
+            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv, hp, walk);
             tiles[3 * w + 0] = c.qt;
             tiles[3 * w + 1] = c.b;
             tiles[3 * w + 2] = c.h;

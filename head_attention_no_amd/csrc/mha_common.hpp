@@ -39,6 +39,8 @@ struct Params {
     int wph;       // waves per query head: the workgroup's waves / hp
     int n_qtiles;  // ceil(S / query rows per head per workgroup)
     int n_items;   // work items: n_qtiles * B * H / hp (the grid may be smaller)
+    int walk;      // 1: items in walk order (see block_coord), and a grid below
+                   // n_items makes each workgroup walk several
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|
@@ -58,27 +60,44 @@ constexpr float kRescaleLog2 = 8.0f;
 // per-tile barrier while the others work.
 // Hardware dispatches workgroup w to XCD w % 8 as that XCD's (w / 8)-th
 // workgroup. When the (batch, K/V head) groups split evenly over the 8 XCDs,
-// every XCD gets whole groups (so all the query heads that share K/V also
-// share that XCD's L2) and the same mix of tile lengths; within an XCD, and
-// in the fallback order, the longest query tiles (the last ones, under a
-// causal mask) start first.
+// every item of a group runs on one XCD (item w on XCD w % 8), so all the
+// query heads that share K/V also share that XCD's L2. Within an XCD, items
+// are ordered by slot = w / 8:
+//  * launch order (one workgroup per item): longest query tiles (the last
+//    ones, under a causal mask) first, across the XCD's groups, so the
+//    dispatcher's tail is short;
+//  * walk order (a resident grid walking the items in rounds, forward then
+//    back): group by group, each group's query tiles longest first, so the
+//    items in flight on an XCD share few K/V heads; a group's long and short
+//    tiles land in alternate rounds, which keeps the per-workgroup totals
+//    balanced.
+// Without an even split (and in both orders), the longest tiles come first.
 struct TileCoord {
     int qt, b, h;
 };
 
-__host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv, int hp)
+__host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv, int hp,
+                                                 int walk)
 {
-    const int reps = H / Hkv / hp;  // workgroups per (batch, K/V head) and query tile
+    const int reps = H / Hkv / hp;  // items per (batch, K/V head) and query tile
     const int groups = B * Hkv;
     TileCoord c;
     if (groups % 8 == 0) {
         const int x = w % 8, slot = w / 8;
-        const int per_tile = (groups / 8) * reps;
-        const int qi = slot / per_tile;
-        const int rem = slot % per_tile;
-        const int grp = (rem / reps) * 8 + x;
+        int qi, grp_local, r;
+        if (walk) {
+            grp_local = slot / (n_qtiles * reps);
+            qi = (slot / reps) % n_qtiles;
+            r = slot % reps;
+        } else {
+            const int per_tile = (groups / 8) * reps;
+            qi = slot / per_tile;
+            grp_local = (slot % per_tile) / reps;
+            r = slot % reps;
+        }
+        const int grp = grp_local * 8 + x;
         c.b = grp / Hkv;
-        c.h = ((grp % Hkv) * reps + rem % reps) * hp;
+        c.h = ((grp % Hkv) * reps + r) * hp;
         c.qt = n_qtiles - 1 - qi;
     } else {
         const int hg = H / hp, bh = B * hg;
@@ -87,6 +106,29 @@ __host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int
         c.h = (w % hg) * hp;
     }
     return c;
+}
+
+// Key tiles a work item of `rows` query rows visits under mask kind `mask`,
+// on average over the query tiles (a close form for the launch heuristic).
+inline double mean_key_tiles(int mask, int S, int W, int rows, int BN)
+{
+    const double all = (S + BN - 1) / BN;
+    if (mask == kMaskNone) return all;
+    const double seen = mask == kMaskCausal ? S / 2.0 : (W < S / 2.0 ? W : S / 2.0);
+    const double m = (seen + rows) / BN;
+    return m < all ? m : all;
+}
+
+// Whether a call walks its items (walk order, and a resident grid when the
+// items outnumber it): the 16-bit kernel at head dim 128, for items of at
+// most 64 key tiles on average. Walking hides each item's start (its Q rows
+// and first K/V tile arrive during the previous item's last tile) but costs
+// a little per tile; on MI355X it was 6 % faster at window 1024, 1.5 % at
+// causal S = 4096 and 1.4 % slower at causal S = 16384, and slower at every
+// length at head dim 32, which is bound by the vector units.
+inline bool walks(bool bits16, int D, int mask, int S, int W, int rows, int BN)
+{
+    return bits16 && D == 128 && mean_key_tiles(mask, S, W, rows, BN) <= 64.0;
 }
 
 // Tile classification for one wave's 32 rows [r0, r0+31] and keys [k0, k1].

@@ -87,8 +87,8 @@ struct Tile16 {
     // more than the overlap gains).
     static constexpr bool PIPELINE = D == 64 || D == 256;
     // The plain loop can walk several work items per workgroup (prefetching
-    // the next item's Q rows and first K/V tile); the launcher uses that at
-    // D = 128 only.
+    // the next item's Q rows and first K/V tile); calls use that at D = 128
+    // only (walks() in mha_common.hpp).
     static constexpr bool WALK = D == 128;
     static constexpr int PIPE_K_AHEAD = 3;    // K operand reads issued this many MFMAs ahead
     static constexpr int PIPE_V_AHEAD = 4;    // V operand pairs issued this many MFMAs ahead
@@ -196,7 +196,7 @@ struct WaveItem {
 template <int D, int MASK, int BN>
 __device__ inline WaveItem wave_item(const Params &p, int item, int wave, int c32)
 {
-    const TileCoord tc = block_coord(item, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
+    const TileCoord tc = block_coord(item, p.n_qtiles, p.B, p.H, p.Hkv, p.hp, p.walk);
     const int rows = 32 * p.wph;  // query rows per head in the workgroup
     WaveItem it;
     it.b = tc.b;
@@ -623,7 +623,7 @@ void mha_fwd16(Params p)
         // the next item's first K/V tile and Q fragments are already on the
         // way.
         const int n_slot = gridDim.x / 8, xcd = blockIdx.x % 8, slot0 = blockIdx.x / 8;
-        const bool walk = TL::WALK && gridDim.x % 8 == 0 && (int)gridDim.x < p.n_items;
+        const bool walk = TL::WALK && p.walk && gridDim.x % 8 == 0 && (int)gridDim.x < p.n_items;
         auto item_index = [&](int r) {
             return (r * n_slot + ((r & 1) ? n_slot - 1 - slot0 : slot0)) * 8 + xcd;
         };

@@ -55,7 +55,7 @@ void mha_fwd32(Params p)
     const int c32 = lane & 31;
     const int g = lane >> 5;
 
-    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp);
+    const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp, 0);
     const int b = tc.b, kvh = tc.h / p.rep;
     const int h = tc.h + wave / p.wph;  // this wave's query head
     const int rows = 32 * p.wph;        // query rows per head in this workgroup

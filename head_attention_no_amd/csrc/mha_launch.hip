@@ -4,7 +4,6 @@
 #include "mha_launch.hpp"
 
 #include <atomic>
-#include <cmath>
 #include <type_traits>
 
 #include "mha_fwd16.hpp"
@@ -40,17 +39,6 @@ int resident_workgroups(const void *kernel, int threads, std::atomic<int> (&cach
     return n;
 }
 
-// Key tiles a work item of `rows` query rows visits, on average over the
-// query tiles (close form; only a launch heuristic uses it).
-template <int MASK>
-double mean_key_tiles(int S, int W, int rows, int BN)
-{
-    const double all = (S + BN - 1) / BN;
-    if (MASK == kMaskNone) return all;
-    const double seen = MASK == kMaskCausal ? S / 2.0 : std::fmin((double)W, S / 2.0);
-    return std::fmin(all, (seen + rows) / BN);
-}
-
 template <typename T, int D, int MASK>
 hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
 {
@@ -62,17 +50,12 @@ hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
         const void *kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK>);
         constexpr int threads = 64 * Tile16<D>::NW;
         int grid = n_items;
-        // The plain-loop kernel can walk several work items per workgroup:
-        // the grid is then the resident workgroup count rounded down to a
-        // multiple of 8 (the XCDs). Walking hides each item's start (its Q
-        // rows and first K/V tile arrive during the previous item's last
-        // tile) but costs a little per tile, so it is used where items are
-        // short: at D = 128, items of at most 64 key tiles on average (MI355X:
-        // 6 % faster at window 1024, 1.5 % at causal S = 4096, 1.4 % slower
-        // at causal S = 16384). At D = 32, bound by the vector units, it
-        // was slower at every length measured.
+        // A walking call (p.walk, set by the C-ABI layer for short items at
+        // D = 128) launches the resident workgroup count rounded down to a
+        // multiple of 8 (the XCDs) when the items outnumber it; each
+        // workgroup then walks several items.
         if constexpr (Tile16<D>::WALK) {
-            if (mean_key_tiles<MASK>(p.S, p.window, 32 * p.wph, Tile16<D>::BN) <= 64.0) {
+            if (p.walk) {
                 static std::atomic<int> cache[kMaxDevices];
                 const int slots = resident_workgroups(kernel, threads, cache) / 8 * 8;
                 if (slots > 0 && slots < n_items) grid = slots;

@@ -112,24 +112,30 @@ const char *fa355_version(void);
 
 /*
  * Work decomposition of one mha_no_cache call, for inspection and tests;
- * pure host arithmetic, no HIP call. A workgroup computes the same block_m
+ * pure host arithmetic, no HIP call. The arguments B ... dtype, mask_kind
+ * and window are those of the call. A work item computes the same block_m
  * query rows of heads_per_wg consecutive query heads, which share one K/V
  * head (heads_per_wg is the largest of 8, 4, 2, 1 that divides H / Hkv and
- * fits the kernel's waves), against key tiles of block_n keys. Given the
- * call's shape, reports the number of such work items (num_workgroups) and,
- * for each of the first `n` item indices, in the longest-first order the
- * library launches them, what it computes: tiles[3*w + 0] = query tile (rows
- * tile*block_m ... tile*block_m + block_m - 1), tiles[3*w + 1] = b,
- * tiles[3*w + 2] = first head h (heads h ... h + heads_per_wg - 1). The
- * library launches one workgroup per item, or, for short items at head dim
- * 128, as many workgroups as the device holds at once (a multiple of 8),
- * each taking several items in a fixed order. Any output pointer may be
- * NULL; `tiles` NULL queries only the sizes.
+ * fits the kernel's waves), against key tiles of block_n keys. Reports the
+ * number of work items (num_workgroups), whether the call walks them
+ * (walk: 0 or 1) and, for each of the first `n` item indices, what it
+ * computes: tiles[3*w + 0] = query tile (rows tile*block_m ...
+ * tile*block_m + block_m - 1), tiles[3*w + 1] = b, tiles[3*w + 2] = first
+ * head h (heads h ... h + heads_per_wg - 1).
+ * Item w runs on XCD w % 8 where the (batch, K/V head) groups split evenly
+ * over the 8 XCDs (all of a group's items on one XCD). A call that does not
+ * walk launches one workgroup per item, longest query tiles first. A
+ * walking call (16-bit inputs at head dim 128, items of at most 64 key
+ * tiles on average) orders each XCD's items group by group, and launches
+ * as many workgroups as the device holds at once (a multiple of 8), each
+ * taking several items in rounds, when the items outnumber them. Any output
+ * pointer may be NULL; `tiles` NULL queries only the sizes.
  * Returns FA355_OK or FA355_ERR_INVALID_ARG / FA355_ERR_UNSUPPORTED under
  * the same rules as mha_no_cache.
  */
-int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int *num_workgroups, int *block_m,
-               int *block_n, int *heads_per_wg, int *tiles, int n);
+int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int mask_kind, int window,
+               int *num_workgroups, int *block_m, int *block_n, int *heads_per_wg, int *walk,
+               int *tiles, int n);
 
 /*
  * fa355_topk: the top-K token sampler of the recipe page "Custom

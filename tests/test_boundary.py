@@ -70,23 +70,25 @@ def test_unsupported_arguments(over):
 
 
 @pytest.mark.parametrize("shape", [
-    (2, 4096, 32, 8, 128, fa.BF16),   # (batch, K/V head) groups split over the 8 XCDs; 4 heads packed
-    (4, 2048, 32, 32, 128, fa.BF16),  # MHA: one head per workgroup
-    (1, 8192, 32, 8, 128, fa.BF16),
-    (1, 16384, 16, 16, 64, fa.F16),
-    (1, 128, 4, 4, 64, fa.F32),       # 4 groups: fallback order
-    (3, 300, 6, 2, 64, fa.BF16),      # ragged S, 3 heads per K/V head: no packing
-    (1, 1, 1, 1, 128, fa.F16),
-    (2, 1000, 8, 2, 32, fa.BF16),     # 4 heads per K/V head
-    (1, 777, 8, 8, 256, fa.F16),      # 4-wave workgroups at D = 256
-    (1, 300, 4, 2, 256, fa.F32),      # 2 heads packed into a 4-wave workgroup
-    (2, 500, 16, 1, 64, fa.BF16),     # 16 heads per K/V head: 8 packed (one per wave)
-    (1, 640, 32, 4, 128, fa.F32),     # 8 heads per K/V head, 4-wave workgroups: 4 packed
-    (2, 96, 12, 6, 256, fa.BF16),     # 2 packed at D = 256
+    (2, 4096, 32, 8, 128, fa.BF16, "causal", -1),   # groups split over the 8 XCDs; 4 heads packed; walks
+    (4, 2048, 32, 32, 128, fa.BF16, "causal", -1),  # MHA: one head per workgroup; walks
+    (1, 8192, 32, 8, 128, fa.BF16, "window", 1024),  # walks
+    (1, 16384, 32, 8, 128, fa.BF16, "causal", -1),  # long items: no walk
+    (1, 16384, 16, 16, 64, fa.F16, "none", -1),
+    (1, 128, 4, 4, 64, fa.F32, "none", -1),         # 4 groups: fallback order
+    (3, 300, 6, 2, 64, fa.BF16, "causal", -1),      # ragged S, 3 heads per K/V head: no packing
+    (1, 300, 6, 2, 128, fa.F16, "causal", -1),      # 2 groups: fallback order, walking
+    (1, 1, 1, 1, 128, fa.F16, "none", -1),
+    (2, 1000, 8, 2, 32, fa.BF16, "none", -1),       # 4 heads per K/V head
+    (1, 777, 8, 8, 256, fa.F16, "none", -1),        # 4-wave workgroups at D = 256
+    (1, 300, 4, 2, 256, fa.F32, "none", -1),        # 2 heads packed into a 4-wave workgroup
+    (2, 500, 16, 1, 64, fa.BF16, "none", -1),       # 16 heads per K/V head: 8 packed (one per wave)
+    (1, 640, 32, 4, 128, fa.F32, "none", -1),       # 8 heads per K/V head, 4-wave workgroups: 4 packed
+    (2, 96, 12, 6, 256, fa.BF16, "none", -1),       # 2 packed at D = 256
 ])
 def test_plan_covers_every_tile_once(shape):
-    B, S, H, Hkv, D, dt = shape
-    pl = fa.plan(B, S, H, Hkv, D, dt, with_tiles=True)
+    B, S, H, Hkv, D, dt, mask, window = shape
+    pl = fa.plan(B, S, H, Hkv, D, dt, mask, window, with_tiles=True)
     waves = 4 if dt == fa.F32 or D == 256 else 8
     hp = max(x for x in (1, 2, 4, 8) if x <= waves and (H // Hkv) % x == 0)
     assert pl["heads_per_workgroup"] == hp
@@ -97,14 +99,42 @@ def test_plan_covers_every_tile_once(shape):
     tiles = pl["tiles"]
     assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B)
                                    for h in range(0, H, hp))
-    # Longest (last) query tiles are dispatched first.
-    first = tiles[:min(len(tiles), B * H // hp)]
-    assert all(t == nq - 1 for t, _, _ in first)
+    groups = B * Hkv
+    if pl["walk"] and groups % 8 == 0:
+        # Walk order: on each XCD (item w on XCD w % 8), group after group,
+        # each group's query tiles longest first.
+        per_group = nq * (H // Hkv // hp)
+        for x in range(8):
+            seq = tiles[x::8]
+            for i in range(0, len(seq), per_group):
+                block = seq[i:i + per_group]
+                assert len({(b, h // (H // Hkv)) for _, b, h in block}) == 1
+                qts = [t for t, _, _ in block]
+                assert qts == sorted(qts, reverse=True)
+    else:
+        # Longest (last) query tiles are dispatched first.
+        first = tiles[:min(len(tiles), B * H // hp)]
+        assert all(t == nq - 1 for t, _, _ in first)
 
 
-def test_plan_keeps_shared_kv_heads_on_one_xcd():
+@pytest.mark.parametrize("shape,walk", [
+    ((2, 4096, 32, 8, 128, fa.BF16, "causal", -1), 1),
+    ((4, 2048, 32, 32, 128, fa.BF16, "causal", -1), 1),
+    ((1, 8192, 32, 8, 128, fa.BF16, "window", 1024), 1),
+    ((1, 16384, 32, 8, 128, fa.BF16, "causal", -1), 0),
+    ((1, 8192, 32, 8, 128, fa.BF16, "none", -1), 0),
+    ((1, 8192, 32, 8, 128, fa.F32, "window", 1024), 0),
+    ((4, 8192, 16, 16, 32, fa.BF16, "causal", -1), 0),
+    ((1, 16384, 16, 16, 64, fa.F16, "none", -1), 0),
+])
+def test_plan_walks_short_items_at_d128(shape, walk):
+    assert fa.plan(*shape)["walk"] == walk
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_plan_keeps_shared_kv_heads_on_one_xcd(mask):
     B, S, H, Hkv = 2, 4096, 32, 8
-    tiles = fa.plan(B, S, H, Hkv, 128, fa.BF16, with_tiles=True)["tiles"]
+    tiles = fa.plan(B, S, H, Hkv, 128, fa.BF16, mask, with_tiles=True)["tiles"]
     xcd_of_group = {}
     for w, (_, b, h) in enumerate(tiles):
         grp = (b, h // (H // Hkv))
@@ -123,6 +153,9 @@ def test_plan_rejects_like_the_entry_point():
     for D in (16, 48, 96, 512):
         with pytest.raises(fa.FA355Error):
             fa.plan(1, 128, 4, 4, D, fa.BF16)
+    for mask, window in (("window", 0), (7, 1)):
+        with pytest.raises(fa.FA355Error):
+            fa.plan(1, 128, 4, 4, 64, fa.BF16, mask, window)
 
 
 def test_missing_library_fails_loudly(tmp_path):

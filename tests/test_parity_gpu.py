@@ -278,8 +278,9 @@ WALK = [
 def test_walk_over_many_items_whole_output(case):
     B, S, H, Hkv, D, dt, mask, window = case
     note(f"walk case {case}")
-    items = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt])["num_workgroups"]
-    assert items > torch.cuda.get_device_properties(0).multi_processor_count
+    pl = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt], mask, window)
+    assert pl["num_workgroups"] > torch.cuda.get_device_properties(0).multi_processor_count
+    assert pl["walk"] == (D == 128)
     q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + H + D)
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
     fa.attention(*_dev(q, k, v), 1.0 / math.sqrt(D), mask, window, out=out)
