@@ -617,11 +617,12 @@ void mha_fwd16(Params p)
         // Persistent walk: with fewer workgroups than work items (one per
         // resident slot, a multiple of 8), workgroup w takes in round r the
         // item of slot r C + (r even ? w / 8 : C - 1 - w / 8) on its own XCD
-        // (item = 8 slot + w % 8, C = grid / 8), so the longest-first order
-        // is walked forward and back (round lengths balance) and every item
-        // keeps the XCD the item order intends. During an item's last tile
-        // the next item's first K/V tile and Q fragments are already on the
-        // way.
+        // (item = 8 slot + w % 8, C = grid / 8). The item order (group by
+        // group, each group's query tiles longest first) is walked forward,
+        // then back, so a workgroup's long and short items alternate and the
+        // totals balance; every item keeps the XCD the item order intends.
+        // During an item's last tile the next item's first K/V tile and Q
+        // rows are already on the way.
         const int n_slot = gridDim.x / 8, xcd = blockIdx.x % 8, slot0 = blockIdx.x / 8;
         const bool walk = TL::WALK && p.walk && gridDim.x % 8 == 0 && (int)gridDim.x < p.n_items;
         auto item_index = [&](int r) {
