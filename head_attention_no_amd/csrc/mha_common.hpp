@@ -120,15 +120,16 @@ inline double mean_key_tiles(int mask, int S, int W, int rows, int BN)
 }
 
 // Whether a call walks its items (walk order, and a resident grid when the
-// items outnumber it): the 16-bit kernel at head dim 128, for items of at
-// most 64 key tiles on average. Walking hides each item's start (its Q rows
-// and first K/V tile arrive during the previous item's last tile) but costs
-// a little per tile; on MI355X it was 6 % faster at window 1024, 1.5 % at
-// causal S = 4096 and 1.4 % slower at causal S = 16384, and slower at every
-// length at head dim 32, which is bound by the vector units.
+// items outnumber it): the 16-bit kernel at head dim 64 or 128, for items of
+// at most 64 key tiles on average. Walking hides each item's start (its Q
+// rows and first K/V tile arrive during the previous item's last tile) but
+// costs a little per tile. On MI355X at D = 128 it was 6 % faster at window
+// 1024, 1.5 % at causal S = 4096 and 1.4 % slower at causal S = 16384; at
+// D = 64, 8 %-10 % faster on causal and windowed shapes; at head dim 32,
+// which is bound by the vector units, slower at every length.
 inline bool walks(bool bits16, int D, int mask, int S, int W, int rows, int BN)
 {
-    return bits16 && D == 128 && mean_key_tiles(mask, S, W, rows, BN) <= 64.0;
+    return bits16 && (D == 64 || D == 128) && mean_key_tiles(mask, S, W, rows, BN) <= 64.0;
 }
 
 // Tile classification for one wave's 32 rows [r0, r0+31] and keys [k0, k1].

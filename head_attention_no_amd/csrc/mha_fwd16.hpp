@@ -80,16 +80,18 @@ struct Tile16 {
     static constexpr int V_AHEAD = 2 * ND <= 8 ? 2 : 1;  // PV k-steps whose V reads are in flight
     // Software-pipelined key loop (the next tile's S MFMAs interleaved with
     // this tile's softmax, then its PV MFMAs with the next tile's max), in an
-    // issue order fixed at compile time. Measured faster at D = 64 (1 %-2 %)
-    // and D = 256 (one wave per SIMD, so no second wave hides the softmax:
-    // 17 %), slower at D = 32 (bound by the vector units) and D = 128 (held at
-    // the power cap, where the extra S MFMAs of each wave's last tile cost
-    // more than the overlap gains).
-    static constexpr bool PIPELINE = D == 64 || D == 256;
+    // issue order fixed at compile time: used at D = 256, where one wave per
+    // SIMD leaves no second wave to hide the softmax (17 % faster there). The
+    // plain loop, with its counted K reads, is as fast or faster at D = 64
+    // (level unmasked, 1.6 %-5 % faster causal and windowed), and faster at
+    // D = 32 (bound by the vector units) and D = 128 (held at the power cap,
+    // where the extra S MFMAs of each wave's last tile cost more than the
+    // overlap gains).
+    static constexpr bool PIPELINE = D == 256;
     // The plain loop can walk several work items per workgroup (prefetching
-    // the next item's Q rows and first K/V tile); calls use that at D = 128
-    // only (walks() in mha_common.hpp).
-    static constexpr bool WALK = D == 128;
+    // the next item's Q rows and first K/V tile); calls use that at D = 64
+    // and 128 (walks() in mha_common.hpp).
+    static constexpr bool WALK = D == 64 || D == 128;
     static constexpr int PIPE_K_AHEAD = 3;    // K operand reads issued this many MFMAs ahead
     static constexpr int PIPE_V_AHEAD = 4;    // V operand pairs issued this many MFMAs ahead
     static constexpr int PIPE_MAX_DELAY = 3;  // MFMAs between the last S MFMA and its max

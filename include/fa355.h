@@ -125,7 +125,7 @@ const char *fa355_version(void);
  * Item w runs on XCD w % 8 where the (batch, K/V head) groups split evenly
  * over the 8 XCDs (all of a group's items on one XCD). A call that does not
  * walk launches one workgroup per item, longest query tiles first. A
- * walking call (16-bit inputs at head dim 128, items of at most 64 key
+ * walking call (16-bit inputs at head dim 64 or 128, items of at most 64 key
  * tiles on average) orders each XCD's items group by group, and launches
  * as many workgroups as the device holds at once (a multiple of 8), each
  * taking several items in rounds, when the items outnumber them. Any output

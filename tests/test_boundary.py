@@ -126,8 +126,11 @@ def test_plan_covers_every_tile_once(shape):
     ((1, 8192, 32, 8, 128, fa.F32, "window", 1024), 0),
     ((4, 8192, 16, 16, 32, fa.BF16, "causal", -1), 0),
     ((1, 16384, 16, 16, 64, fa.F16, "none", -1), 0),
+    ((2, 4096, 32, 8, 64, fa.BF16, "causal", -1), 1),
+    ((1, 8192, 32, 8, 64, fa.F16, "window", 1000), 1),
+    ((2, 4096, 16, 16, 256, fa.BF16, "causal", -1), 0),
 ])
-def test_plan_walks_short_items_at_d128(shape, walk):
+def test_plan_walks_short_items_at_d64_d128(shape, walk):
     assert fa.plan(*shape)["walk"] == walk
 
 

@@ -264,13 +264,15 @@ def test_rows_past_the_end_are_never_used(dt, D, mask):
 
 WALK = [
     # B, S, H, Hkv, D, dtype, mask, window: more work items than the GPU holds
-    # workgroups. At D = 128 with short items each workgroup walks several
-    # items, the last round only partly filled; the D = 32 case launches one
-    # workgroup per item.
+    # workgroups. At D = 64 and 128 with short items each workgroup walks
+    # several items, the last round only partly filled; the D = 32 case
+    # launches one workgroup per item.
     (2, 1100, 32, 8, 128, "bf16", "causal", -1),
     (1, 1100, 64, 8, 128, "bf16", "sliding_window", 200),
     (2, 1037, 32, 8, 128, "f16", "none", -1),
     (1, 600, 128, 128, 32, "bf16", "causal", -1),
+    (2, 1100, 32, 8, 64, "f16", "causal", -1),
+    (1, 1500, 64, 16, 64, "bf16", "sliding_window", 150),
 ]
 
 
@@ -280,7 +282,7 @@ def test_walk_over_many_items_whole_output(case):
     note(f"walk case {case}")
     pl = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt], mask, window)
     assert pl["num_workgroups"] > torch.cuda.get_device_properties(0).multi_processor_count
-    assert pl["walk"] == (D == 128)
+    assert pl["walk"] == (D in (64, 128))
     q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + H + D)
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
     fa.attention(*_dev(q, k, v), 1.0 / math.sqrt(D), mask, window, out=out)
