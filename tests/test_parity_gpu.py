@@ -272,6 +272,7 @@ WALK = [
     (2, 1037, 32, 8, 128, "f16", "none", -1),
     (1, 600, 128, 128, 32, "bf16", "causal", -1),
     (2, 1100, 32, 8, 64, "f16", "causal", -1),
+    (4, 1100, 32, 8, 64, "f16", "causal", -1),    # 576 items: three rounds on 256 workgroups
     (1, 1500, 64, 16, 64, "bf16", "sliding_window", 150),
 ]
 
