@@ -291,3 +291,36 @@ def test_walk_over_many_items_whole_output(case):
     got = out.cpu()
     assert not torch.isnan(got.float()).any(), "some output element was never written"
     check(got, oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask, window), dt, str(case))
+
+
+@pytest.mark.parametrize("case", [
+    (2, 1100, 32, 8, 128, "bf16", "causal", -1),           # walks: resident grid, several items each
+    (1, 700, 16, 16, 64, "f16", "sliding_window", 100),    # walks at D = 64
+    (1, 500, 8, 2, 256, "bf16", "none", -1),                # pipelined loop
+])
+def test_graph_replays_match_eager(case):
+    """The call captured in a HIP graph (torch.cuda.CUDAGraph) replays to the
+    eager result bit for bit, replay after replay, with eager work and
+    synchronisations in between. The kernels record no memset nodes."""
+    B, S, H, Hkv, D, dt, mask, window = case
+    note(f"graph case {case}")
+    q, k, v = _dev(*inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + D))
+    scale = 1.0 / math.sqrt(D)
+    eager = fa.attention(q, k, v, scale, mask, window)
+    out = torch.full_like(q, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.attention(q, k, v, scale, mask, window, out=out)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.attention(q, k, v, scale, mask, window, out=out)
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager result"
+        fa.attention(q, k, v, scale, mask, window)  # eager work between replays
