@@ -13,8 +13,9 @@
  * S x S score matrix is never stored.
  *
  * C ABI only: plain pointers and sizes, no C++ or framework types. All
- * functions are thread-safe; the library keeps no per-call state and
- * allocates no device memory.
+ * functions are thread-safe; the library keeps no per-call state (only
+ * per-device caches of the architecture check and of how many workgroups
+ * the device holds at once) and allocates no device memory.
  */
 #ifndef FA355_H
 #define FA355_H
