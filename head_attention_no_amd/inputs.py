@@ -87,6 +87,18 @@ def make_qkv(B: int, S: int, H: int, Hkv: int, D: int, dtype: str = "bf16", seed
     return q.to(td), k.to(td), v.to(td)
 
 
+def make_qkv_device(B: int, S: int, H: int, Hkv: int, D: int, dtype: str, seed: int, device):
+    """The make_qkv recipe drawn on `device` with a seeded device generator
+    (other values than the CPU draw of the same seed), for tensors too large
+    to draw on the host quickly; checks copy the slices they need back."""
+    g = torch.Generator(device).manual_seed(int(seed))
+    td = DTYPES[dtype]
+    q = torch.randn(B, S, H, D, generator=g, dtype=torch.float32, device=device).to(td)
+    k = torch.randn(B, S, Hkv, D, generator=g, dtype=torch.float32, device=device).to(td)
+    v = torch.randn(B, S, Hkv, D, generator=g, dtype=torch.float32, device=device).to(td)
+    return q, k, v
+
+
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.S, w.H, w.Hkv, w.D, w.dtype, w.seed, w.k_mult)
 

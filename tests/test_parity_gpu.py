@@ -324,3 +324,35 @@ def test_graph_replays_match_eager(case):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs from the eager result"
         fa.attention(q, k, v, scale, mask, window)  # eager work between replays
+
+
+@pytest.mark.parametrize("case", [
+    # q and out of 2 GiB each: element and byte offsets past 32 bits.
+    (4, 32768, 64, 8, 128, "bf16", "causal", -1),
+    # one batch's K (and V) of 1 GiB: S = 65536 rows of 64 heads.
+    (1, 65536, 64, 64, 128, "bf16", "causal", -1),
+])
+def test_large_tensors_sampled_rows(case):
+    """Tensors at the sizes where offsets outgrow 32 bits; a sample of rows
+    (both batch ends, several heads, both sequence ends and the middle) is
+    recomputed by the oracle from the slices each row needs."""
+    B, S, H, Hkv, D, dt, mask, window = case
+    note(f"large case {case}")
+    q, k, v = inputs.make_qkv_device(B, S, H, Hkv, D, dt, seed=S + H, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out = fa.attention(q, k, v, scale, mask, window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rep = H // Hkv
+    errs = []
+    for b in sorted({0, B - 1}):
+        for h in sorted({0, H - 1, int(rng.integers(H))}):
+            g = h // rep
+            qs = q[b:b + 1, :, h:h + 1].contiguous().cpu()
+            ks = k[b:b + 1, :, g:g + 1].contiguous().cpu()
+            vs = v[b:b + 1, :, g:g + 1].contiguous().cpu()
+            idx = sorted({0, 1, 63, 64, S // 2, S - 2, S - 1} | set(rng.integers(0, S, 6).tolist()))
+            want = oracle.attention_rows(qs, ks, vs, scale, mask, window, [(0, 0, i) for i in idx])
+            got = out[b, idx, h].cpu()
+            errs.append(check(got, want, dt, f"{case} b={b} h={h}"))
+    note(f"  worst max {max(e[0] for e in errs):.3e}")
