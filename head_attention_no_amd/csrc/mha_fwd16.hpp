@@ -64,11 +64,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 // with the 512-register budget), and the LDS swizzle periods (below).
 template <int D>
 struct Tile16 {
-    static constexpr int BN = D == 32 ? 128 : D == 256 ? 64 : 8192 / D;  // keys per tile: 128, 128, 64, 64
+    static constexpr int BN = D == 32 ? 128 : 64;  // keys per tile: 128 at D = 32, else 64
     static constexpr int NW = D == 256 ? 4 : 8;           // waves per workgroup, 32 query rows each
-    // Waves per SIMD: D = 32, bound by the vector units and at 120 registers,
-    // runs two workgroups per CU (4 waves per SIMD: 8-20 % faster than 2).
-    static constexpr int WPE = D == 256 ? 1 : D == 32 ? 4 : 2;
+    // Waves per SIMD: D = 32 and 64, bound by the vector units and at 120
+    // registers (64-key tiles at D = 64), run two workgroups per CU (4 waves
+    // per SIMD: 8-20 % faster than 2 at D = 32, 3-7 % at D = 64).
+    static constexpr int WPE = D == 256 ? 1 : D <= 64 ? 4 : 2;
     static constexpr int NKT = BN / 32;           // 32-key sub-tiles of S^T
     static constexpr int ND = D / 32;             // 32-dim sub-tiles of O^T
     static constexpr int G = 512 / D;             // keys per 1 KiB key group

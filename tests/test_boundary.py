@@ -93,7 +93,7 @@ def test_plan_covers_every_tile_once(shape):
     hp = max(x for x in (1, 2, 4, 8) if x <= waves and (H // Hkv) % x == 0)
     assert pl["heads_per_workgroup"] == hp
     assert pl["block_m"] == 32 * waves // hp
-    assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 128, 128: 64, 256: 64}[D])
+    assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 64, 128: 64, 256: 64}[D])
     nq = -(-S // pl["block_m"])
     assert pl["num_workgroups"] == nq * B * H // hp
     tiles = pl["tiles"]

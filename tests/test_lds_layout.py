@@ -17,7 +17,7 @@ import pytest
 
 
 DIMS = [32, 64, 128, 256]
-TILE_KEYS = {32: 128, 64: 128, 128: 64, 256: 64}
+TILE_KEYS = {32: 128, 64: 64, 128: 64, 256: 64}
 K_BASES = {32: 1, 64: 1, 128: 2, 256: 4}      # k-step period of the K read bases
 V_BASES = {32: (1, 2), 64: (1, 1), 128: (1, 1), 256: (2, 1)}  # (sub-tile, half) periods
 
