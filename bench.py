@@ -179,6 +179,37 @@ def time_gpu(w, steps: int, warmup: int):
     }
 
 
+FLUSH_MIB = 512  # larger than the L2s (4 MiB per XCD) and the 256 MiB MALL together
+
+
+def time_cold(w, steps: int):
+    """The kernel with cold caches: before each launch a 512 MiB buffer is
+    written, which evicts q, k, v and out from the L2s and the MALL; HIP
+    events on the kernel's stream bracket the launch alone."""
+    import torch
+
+    import head_attention_no_amd as fa
+    from head_attention_no_amd import inputs
+
+    q, k, v = (x.cuda() for x in inputs.workload_qkv(w))
+    out = torch.empty_like(q)
+    flush = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (s, e) in enumerate(ev):
+        flush.fill_(i & 0xFF)
+        s.record(stream)
+        fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in ev)
+    mean = sum(ms) / len(ms)
+    return {"launches": steps, "flush_bytes_before_each": FLUSH_MIB << 20,
+            "launch_ms_mean": round(mean, 5), "launch_ms_median": round(ms[len(ms) // 2], 5),
+            "tflops_mean": round(flops(w) / (mean * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The fp64 oracle on a bounded sample: whole K/V head groups (one K/V
     head and its H/Hkv query heads), batch by batch, until the time budget is
@@ -525,12 +556,14 @@ def main():
     print(f"# timing {w.name}: {args.warmup} warmup + {args.steps} steps", file=sys.stderr,
           flush=True)
     t = time_gpu(w, args.steps, args.warmup)
+    cold = time_cold(w, max(10, min(args.steps, 30)))
     line = None
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle sample)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
     line = one_line(w, args, t, cpu)
+    line["cold_cache"] = cold
     if args.all:
         others = {}
         for o in inputs.WORKLOADS + inputs.WIDER:

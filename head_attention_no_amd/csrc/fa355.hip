@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -22,16 +23,23 @@ namespace {
 
 using fa355::Params;
 
+constexpr double kLog2e = 1.4426950408889634;
+
 const char *const kStatusText[] = {
     "success",
     "invalid argument (null pointer, size < 1, H not a multiple of Hkv, unknown dtype or mask, "
-    "window < 1 with the sliding mask, non-finite scale, or out overlapping an input)",
-    "unsupported (head dim other than 32, 64, 128 or 256, pointer not 16-byte aligned, grid too large, or one K/V head slice of 2 GiB or more)",
+    "window < 1 with the sliding mask, non-finite scale or |scale| * log2(e) beyond the fp32 range, "
+    "or out overlapping an input)",
+    "unsupported (head dim other than 32, 64, 128 or 256, pointer not 16-byte aligned, grid too large, "
+    "or one token row of q over 16 MiB)",
     "no usable device (no current HIP device, or it is not gfx950)",
     "kernel launch failed",
 };
 
 int elem_size(int dtype) { return dtype == FA355_F32 ? 4 : 2; }
+
+// Largest token row of q (H * D elements; k and v rows are no longer).
+constexpr int64_t kMaxRowBytes = (int64_t)1 << 24;
 
 bool overlaps(const void *a, int64_t na, const void *b, int64_t nb)
 {
@@ -84,9 +92,11 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     const int rep = H / Hkv;
     const int64_t n_qtiles = ((int64_t)S + block_m(dtype, D, rep) - 1) / block_m(dtype, D, rep);
     if (n_qtiles * B * (H / heads_per_wg(dtype, D, rep)) > INT32_MAX) return FA355_ERR_UNSUPPORTED;
-    // The 16-bit kernel addresses one (batch, K/V head) slice with 32-bit
-    // byte offsets: S rows of Hkv * D elements must stay below 2 GiB.
-    if ((int64_t)S * Hkv * D * elem_size(dtype) >= ((int64_t)1 << 31)) return FA355_ERR_UNSUPPORTED;
+    // Buffer offsets inside one tile are 32-bit: a tile spans at most 128
+    // token rows of K/V and 32 of Q, so one token's row of q (H * D
+    // elements) or of k / v (Hkv * D elements) may hold at most 16 MiB.
+    // Every offset across tokens, heads and batches is 64-bit.
+    if ((int64_t)H * D * elem_size(dtype) > kMaxRowBytes) return FA355_ERR_UNSUPPORTED;
     return FA355_OK;
 }
 
@@ -155,7 +165,9 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     int rc = check_shape(B, S, H, Hkv, D, dtype);
     if (rc == FA355_ERR_INVALID_ARG) return rc;
     if (check_mask(mask_kind, window) != FA355_OK) return FA355_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return FA355_ERR_INVALID_ARG;
+    // |scale| * log2(e) is the kernels' fp32 exponent scale: it must be finite.
+    if (!std::isfinite(scale) || std::fabs((double)scale) * kLog2e > (double)FLT_MAX)
+        return FA355_ERR_INVALID_ARG;
     const int64_t es = elem_size(dtype);
     const int64_t q_bytes = (int64_t)B * S * H * D * es;
     const int64_t kv_bytes = (int64_t)B * S * Hkv * D * es;
@@ -190,7 +202,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     // A scale below 1e-30 in magnitude is taken as 1e-30: for any fp32 score
     // |s| < 1e20 the exponent then stays below 1e-10 and exp2 rounds to
     // exactly 1, as with scale 0, while hidden scores (-inf) still give 0.
-    p.scale_log2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
+    p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * kLog2e, 1e-30);
     const bool neg = std::signbit(scale) && scale != 0.0f;
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
 

@@ -281,8 +281,10 @@ void mha_fwd16(Params p)
     }
     auto tile_rsrc = [&](const uint8_t *base, int kt) {
         const int k0 = kt * BN;
-        // The resource covers rows k0 .. S-1 only; later rows read as zero.
-        const int nrec = (S - 1 - k0) * (int)kv_stride + D * 2;
+        // The resource covers the tile's own rows k0 .. min(k0 + BN, S) - 1
+        // (at most BN rows, so the range fits 32 bits whatever the size of
+        // the tensor); rows past the end of the sequence read as zero.
+        const int nrec = (min(BN, S - k0) - 1) * (int)kv_stride + D * 2;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base) + (int64_t)k0 * kv_stride,
                                                  0, nrec, kRsrcWord3);
     };

@@ -61,20 +61,27 @@ typedef enum {
  * mha_no_cache: out = softmax(mask(scale * q k^T)) v, per batch and head.
  *
  * Arguments (all device pointers on the current HIP device, contiguous):
- *   out  [B, S, H,   D]  written; same shape and dtype as q ("output ...
- *                        with the same shape as q", page section "Args").
+ *   out  [B, S, H,   D]  written; shaped like q (the page's "Args"
+ *                        section fixes the shape) and of q's dtype.
  *   q    [B, S, H,   D]  queries, BSHD.
  *   k    [B, S, Hkv, D]  keys, BSHD, or BShD with Hkv < H for grouped
  *                        attention (page, grouped attention, "Step -1").
- *   v    [B, S, Hkv, D]  values, same layout as k ("both key and value
- *                        must be BShD if one is").
+ *   v    [B, S, Hkv, D]  values, in k's layout: the page's grouped
+ *                        attention section requires k and v to carry the
+ *                        same head count.
  *   B, S, H, Hkv, D      batch, sequence length (queries and keys: there is
  *                        no cache), query heads, K/V heads, head dim.
  *                        H must be a multiple of Hkv; query head h reads
  *                        K/V head h / (H / Hkv) (contiguous groups, the
  *                        reading taken of the page's "G groups").
  *   scale                multiplies q.k before the mask (page, Step 3);
- *                        any finite value, 0 and negatives included.
+ *                        any finite value with |scale| * log2(e) within
+ *                        the fp32 range (|scale| up to about 2.36e38), 0 and
+ *                        negatives included. The scores are formed in
+ *                        fp32 as (q.k) * |scale| * log2(e), so every
+ *                        |scale * q.k| must stay below FLT_MAX / log2(e)
+ *                        (about 2.36e38); larger products are outside the
+ *                        contract (the result is then undefined).
  *   mask_kind            an fa355_mask value.
  *   window               sliding-window width (>= 1) for
  *                        FA355_MASK_SLIDING_WINDOW; ignored otherwise.
@@ -84,7 +91,10 @@ typedef enum {
  *
  * Supported today: D in {32, 64, 128, 256}; any S >= 1 (ragged tails are
  * masked); all three dtypes. Pointers must be 16-byte aligned; out must not overlap
- * q, k or v. Element offsets are computed in 64 bits.
+ * q, k or v. Offsets across tokens, heads and batches are 64-bit, so q, k,
+ * v and out may be of any size; only one token's row of q (H * D
+ * elements) is limited, to 16 MiB, because offsets inside one tile are
+ * 32-bit.
  *
  * Ownership: the caller owns every buffer; the library reads q, k, v and
  * writes every element of out, and allocates nothing.
@@ -97,8 +107,10 @@ typedef enum {
  * before any HIP call, so an invalid call touches no device state:
  * FA355_ERR_INVALID_ARG for a null pointer, a size < 1, H % Hkv != 0, an
  * unknown dtype or mask, window < 1 with the sliding mask, a non-finite
- * scale, or out overlapping an input; FA355_ERR_UNSUPPORTED for another D,
- * a misaligned pointer or a grid too large to launch; FA355_ERR_DEVICE if
+ * scale or one with |scale| * log2(e) beyond the fp32 range, or out
+ * overlapping an input; FA355_ERR_UNSUPPORTED for another D, a misaligned
+ * pointer, a grid too large to launch (more than 2^31 - 1 work items) or
+ * a token row of q over 16 MiB; FA355_ERR_DEVICE if
  * no HIP device is current or it is not gfx950; FA355_ERR_LAUNCH if the
  * launch fails.
  */

@@ -52,6 +52,7 @@ def call(**over):
     dict(mask_kind=fa.MASK_SLIDING_WINDOW, window=0),
     dict(mask_kind=fa.MASK_SLIDING_WINDOW, window=-1),
     dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(scale=3.0e38), dict(scale=-2.4e38),  # |scale| * log2(e) beyond the fp32 range
     dict(out=P2 + 64),                 # out overlaps q
     dict(out=P3 - 32),                 # out runs into k
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
@@ -64,9 +65,30 @@ def test_invalid_arguments(over):
     dict(q=P2 + 2), dict(out=P1 + 8), dict(k=P3 + 4), dict(v=P4 + 1),
     dict(B=1 << 12, S=1 << 17, H=1 << 10, Hkv=1 << 10, out=1 << 47, q=2 << 47, k=3 << 47,
          v=4 << 47),                  # 2^32 workgroups
+    dict(H=1 << 17, Hkv=1 << 17, D=128, out=1 << 47, q=2 << 47, k=3 << 47,
+         v=4 << 47),                  # one token row of q: 32 MiB
 ], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
 def test_unsupported_arguments(over):
     assert call(**over) == fa.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over", [
+    dict(scale=2.3e38), dict(scale=-2.3e38), dict(scale=1e-45), dict(scale=-0.0),
+    # K and V of one batch at 4 GiB each (S = 2^20 rows of 16 heads): sizes
+    # past 32 bits are accepted; only one token row of q is limited.
+    dict(B=1, S=1 << 20, H=16, Hkv=16, D=128, out=1 << 44, q=2 << 44, k=3 << 44, v=4 << 44),
+    dict(H=1 << 15, Hkv=1 << 15, D=256, out=1 << 47, q=2 << 47, k=3 << 47,
+         v=4 << 47),                  # one token row of q: exactly 16 MiB
+], ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_valid_arguments_reach_the_device_check(over):
+    """Calls that pass every argument check go on to the device check, which
+    fails here (no GPU): validation accepted them. The addresses are fake, so
+    this must never run where a device is present."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present: the fake addresses would be launched")
+    assert call(**over) == fa.ERR_DEVICE
 
 
 @pytest.mark.parametrize("shape", [

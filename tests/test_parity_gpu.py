@@ -106,6 +106,23 @@ def test_workload_small_fp32_whole_output():
     note(f"  max {mx:.3e} mean {mean:.3e}")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", inputs.WORKLOADS[1:], ids=lambda w: w.name)
+def test_workload_whole_output(w):
+    """The four full-size workloads, launched exactly as the benchmark
+    launches them, against the fp64 oracle over every output element: max
+    and mean absolute error over the whole output."""
+    note(f"workload {w.name} (whole output)")
+    q, k, v = inputs.workload_qkv(w)
+    got = run_gpu(q, k, v, w.scale, w.mask, w.window)
+    want = oracle.attention(q, k, v, w.scale, w.mask, w.window)
+    err = np.abs(got.to(torch.float64).numpy() - want)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    note(f"  {err.size} elements: max {err.max():.3e} at (b, s, h, d) = {tuple(int(x) for x in worst)}, "
+         f"mean {err.mean():.3e}")
+    mx, mean = check(got, want, w.dtype, w.name)
+
+
 def sample_rows(w, n_heads=6, seed=0):
     """(b, h, i) triples: tile edges, both ends, and random rows of a few heads."""
     rng = np.random.default_rng(seed)
@@ -120,7 +137,7 @@ def sample_rows(w, n_heads=6, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("w", inputs.WORKLOADS[1:] + inputs.WIDER, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", inputs.WIDER, ids=lambda w: w.name)
 def test_workload_full_size_sampled_rows(w):
     """Full-size workloads, launched exactly as the benchmark launches them;
     the oracle recomputes a sample of rows one by one."""
@@ -186,14 +203,53 @@ def test_grouped_equals_repeated_heads(mask, window):
     assert torch.equal(grouped, rep)
 
 
-def test_key_shift_invariance_fp32():
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_key_shift_large_scores(dt):
     """A constant vector added to every key shifts each score row by a
-    constant (here several hundred), which the running max must absorb."""
-    q, k, v = inputs.make_qkv(1, 260, 2, 2, 64, "f32", seed=9)
+    constant of several hundred, which the running max must absorb (a
+    softmax without the max subtraction overflows). Both sides get the same
+    shifted keys, rounded to the input dtype."""
+    q, k, v = inputs.make_qkv(1, 260, 2, 2, 64, dt, seed=9)
     u = torch.randn(64, generator=torch.Generator().manual_seed(1)) * 60.0
-    got = run_gpu(q, k + u, v, 1.0 / 8, "causal", -1)
-    want = oracle.attention(q, k, v, 1.0 / 8, "causal", -1)
-    check(got, want, "f32", "key shift")
+    ks = (k.float() + u).to(k.dtype)
+    shift = (q.double()[0, :, 0] @ u.double()) / 8
+    assert shift.abs().max() > 200, "the case must shift some score rows by hundreds"
+    got = run_gpu(q, ks, v, 1.0 / 8, "causal", -1)
+    want = oracle.attention(q, ks, v, 1.0 / 8, "causal", -1)
+    check(got, want, dt, f"key shift {dt}")
+
+
+@pytest.mark.parametrize("dt,mask,window", [("bf16", "causal", -1), ("f16", "none", -1),
+                                            ("bf16", "sliding_window", 300)])
+def test_growing_scores_raise_the_running_max(dt, mask, window):
+    """Keys whose magnitude grows along the sequence (k_j (1 + 3 (j // 64)))
+    make a row's score maximum climb tile after tile, by more than the 2^8
+    slack the kernels allow before they raise the running max and rescale O
+    and l. The case checks on the CPU that every row of one head sees such
+    climbs, then compares the GPU with the oracle on the same rounded
+    inputs."""
+    B, S, H, Hkv, D = 1, 1000, 4, 2, 128
+    q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=21)
+    ramp = (1 + 3 * (torch.arange(S) // 64)).to(torch.float32)[None, :, None, None]
+    kr = (k.float() * ramp).to(k.dtype)
+    scale = 1.0 / math.sqrt(D)
+    # log2-unit score maxima per 64-key tile for query head 0, rows past 900.
+    sc = (q.double()[0, 900:, 0] @ kr.double()[0, :, 0].T) * scale / math.log(2)
+    tile_max = sc[:, :896].reshape(sc.shape[0], 14, 64).amax(dim=2)
+    climbs = (tile_max[:, 1:] - torch.cummax(tile_max, dim=1).values[:, :-1] > 8).sum(dim=1)
+    assert (climbs >= 3).all(), "the case must make the running max climb"
+    got = run_gpu(q, kr, v, scale, mask, window)
+    check(got, oracle.attention(q, kr, v, scale, mask, window), dt, f"growing scores {dt} {mask}")
+
+
+def test_huge_scale_one_hot():
+    """scale = 1e38 with small inputs: every |scale q.k| stays inside the
+    fp32 range, and the softmax is one-hot on each row's largest score."""
+    q, k, v = inputs.make_qkv(1, 300, 4, 2, 64, "f32", seed=22)
+    q, k = q * 0.02, k * 0.02
+    got = run_gpu(q, k, v, 1e38, "causal", -1)
+    want = oracle.attention(q, k, v, 1e38, "causal", -1)
+    check(got, want, "f32", "scale 1e38")
 
 
 def test_peaky_softmax_fp16_small():
@@ -330,8 +386,10 @@ def test_graph_replays_match_eager(case):
 @pytest.mark.parametrize("case", [
     # q and out of 2 GiB each: element and byte offsets past 32 bits.
     (4, 32768, 64, 8, 128, "bf16", "causal", -1),
-    # one batch's K (and V) of 1 GiB: S = 65536 rows of 64 heads.
-    (1, 65536, 64, 64, 128, "bf16", "causal", -1),
+    # one batch's K (and V) of 2 GiB: S = 65536 rows of 128 heads.
+    (1, 65536, 128, 128, 128, "bf16", "causal", -1),
+    # fp32 K and V of 2 GiB each (64 K/V heads), q and out of 4 GiB (128 heads).
+    (1, 32768, 128, 64, 256, "f32", "sliding_window", 5000),
 ])
 def test_large_tensors_sampled_rows(case):
     """Tensors at the sizes where offsets outgrow 32 bits; a sample of rows
