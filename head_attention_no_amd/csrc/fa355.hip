@@ -125,6 +125,15 @@ int call_walks(int dtype, int D, int rep, int mask_kind, int S, int window_clamp
                : 0;
 }
 
+// Whether the items are ordered group by group (see fa355::block_coord):
+// calls that walk, and unmasked 16-bit calls (all their items are alike, so
+// nothing is gained by running the longest first, and group order keeps the
+// K/V of the items in flight on an XCD within its L2).
+int call_group_order(int dtype, int mask_kind, int walk)
+{
+    return walk || (dtype != FA355_F32 && mask_kind == FA355_MASK_NONE) ? 1 : 0;
+}
+
 // Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
@@ -209,6 +218,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     const int grid = p.n_qtiles * B * (H / p.hp);
     p.n_items = grid;
     p.walk = call_walks(dtype, D, p.rep, mask_kind, S, p.window);
+    p.group_order = call_group_order(dtype, mask_kind, p.walk);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (dtype) {
@@ -276,7 +286,8 @@ extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int ma
     if (tiles) {
         if (n < 0) return FA355_ERR_INVALID_ARG;
         for (int w = 0; w < n && w < grid; ++w) {
-            const fa355::TileCoord c = fa355::block_coord(w, n_qtiles, B, H, Hkv, hp, walk);
+            const fa355::TileCoord c =
+                fa355::block_coord(w, n_qtiles, B, H, Hkv, hp, call_group_order(dtype, mask_kind, walk));
             tiles[3 * w + 0] = c.qt;
             tiles[3 * w + 1] = c.b;
             tiles[3 * w + 2] = c.h;

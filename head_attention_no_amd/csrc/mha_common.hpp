@@ -39,8 +39,8 @@ struct Params {
     int wph;       // waves per query head: the workgroup's waves / hp
     int n_qtiles;  // ceil(S / query rows per head per workgroup)
     int n_items;   // work items: n_qtiles * B * H / hp (the grid may be smaller)
-    int walk;      // 1: items in walk order (see block_coord), and a grid below
-                   // n_items makes each workgroup walk several
+    int walk;      // 1: a grid below n_items makes each workgroup walk several items
+    int group_order;  // 1: items in group order (see block_coord)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|
@@ -66,18 +66,19 @@ constexpr float kRescaleLog2 = 8.0f;
 //  * launch order (one workgroup per item): longest query tiles (the last
 //    ones, under a causal mask) first, across the XCD's groups, so the
 //    dispatcher's tail is short;
-//  * walk order (a resident grid walking the items in rounds, forward then
-//    back): group by group, each group's query tiles longest first, so the
-//    items in flight on an XCD share few K/V heads; a group's long and short
-//    tiles land in alternate rounds, which keeps the per-workgroup totals
-//    balanced.
-// Without an even split (and in both orders), the longest tiles come first.
+//  * group order (calls that walk, and unmasked 16-bit calls, whose items
+//    are all alike): group by group, each group's query tiles longest
+//    first, so the items in flight on an XCD share few K/V heads and their
+//    K/V stays in its L2. A walking call takes the items in rounds, forward
+//    then back, so a group's long and short tiles land in alternate rounds,
+//    which keeps the per-workgroup totals balanced.
+// Without an even split, the longest tiles come first.
 struct TileCoord {
     int qt, b, h;
 };
 
 __host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int H, int Hkv, int hp,
-                                                 int walk)
+                                                 int group_order)
 {
     const int reps = H / Hkv / hp;  // items per (batch, K/V head) and query tile
     const int groups = B * Hkv;
@@ -85,7 +86,7 @@ __host__ __device__ inline TileCoord block_coord(int w, int n_qtiles, int B, int
     if (groups % 8 == 0) {
         const int x = w % 8, slot = w / 8;
         int qi, grp_local, r;
-        if (walk) {
+        if (group_order) {
             grp_local = slot / (n_qtiles * reps);
             qi = (slot / reps) % n_qtiles;
             r = slot % reps;

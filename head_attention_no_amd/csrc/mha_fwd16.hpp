@@ -201,7 +201,7 @@ struct WaveItem {
 template <int D, int MASK, int BN>
 __device__ inline WaveItem wave_item(const Params &p, int item, int wave, int c32)
 {
-    const TileCoord tc = block_coord(item, p.n_qtiles, p.B, p.H, p.Hkv, p.hp, p.walk);
+    const TileCoord tc = block_coord(item, p.n_qtiles, p.B, p.H, p.Hkv, p.hp, p.group_order);
     const int rows = 32 * p.wph;  // query rows per head in the workgroup
     WaveItem it;
     it.b = tc.b;
@@ -331,19 +331,31 @@ void mha_fwd16(Params p)
 
     const int kt_begin = it0.kt_begin, kt_end = it0.kt_end;
 
-    // Epilogue: O = O^T / l, written back in BSHD.
+    // Epilogue: O = O^T / l, written back in BSHD with 16-byte stores.
+    // Lane (c, g) holds O[c][32t + 8i + 4g .. +3] (4 values, two packed
+    // words w[i][0..1]); lanes c and c + 32 swap halves with
+    // v_permlane32_swap so that lane g = 0 holds the 8 values of groups
+    // i = 0, 1 and lane g = 1 those of i = 2, 3: each lane then stores
+    // 16 contiguous bytes per group. The swap exchanges the upper 32 lanes
+    // of its first operand with the lower 32 lanes of its second.
     auto store_out = [&](const WaveItem &it) {
         const float inv = 1.0f / half_sum(l_run);
-        if (it.row < S) {
-            T *orow = O + ((int64_t)it.b * S + it.row) * q_row_stride + (int64_t)it.h * D;
+        T *orow = O + ((int64_t)it.b * S + it.row) * q_row_stride + (int64_t)it.h * D;
 #pragma unroll
-            for (int t = 0; t < ND; ++t)
+        for (int t = 0; t < ND; ++t) {
+            uint32_t w[4][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x2 w = {pack2<T>(oacc[t][4 * i] * inv, oacc[t][4 * i + 1] * inv),
-                                     pack2<T>(oacc[t][4 * i + 2] * inv, oacc[t][4 * i + 3] * inv)};
-                    *reinterpret_cast<u32x2 *>(orow + 32 * t + 8 * i + 4 * g) = w;
-                }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    w[i][h] = pack2<T>(oacc[t][4 * i + 2 * h] * inv, oacc[t][4 * i + 2 * h + 1] * inv);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(w[i][0], w[i + 2][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(w[i][1], w[i + 2][1], false, false);
+                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                if (it.row < S) *reinterpret_cast<u32x4 *>(orow + 32 * t + 8 * (i + 2 * g)) = v;
+            }
         }
     };
 

@@ -77,11 +77,14 @@ typedef enum {
  *   scale                multiplies q.k before the mask (page, Step 3);
  *                        any finite value with |scale| * log2(e) within
  *                        the fp32 range (|scale| up to about 2.36e38), 0 and
- *                        negatives included. The scores are formed in
- *                        fp32 as (q.k) * |scale| * log2(e), so every
- *                        |scale * q.k| must stay below FLT_MAX / log2(e)
- *                        (about 2.36e38); larger products are outside the
- *                        contract (the result is then undefined).
+ *                        negatives included. The kernels form each
+ *                        exponent in fp32 as (q.k) * |scale| * log2(e)
+ *                        minus the row's running maximum with one fused
+ *                        multiply-add, so every |scale * q.k| * log2(e)
+ *                        must stay below 2^24 (about 1.7e7): beyond that
+ *                        the rounding of the maximum alone exceeds one
+ *                        unit of the exponent, and the result is outside
+ *                        the contract (undefined).
  *   mask_kind            an fa355_mask value.
  *   window               sliding-window width (>= 1) for
  *                        FA355_MASK_SLIDING_WINDOW; ignored otherwise.
@@ -137,12 +140,14 @@ const char *fa355_version(void);
  * head h (heads h ... h + heads_per_wg - 1).
  * Item w runs on XCD w % 8 where the (batch, K/V head) groups split evenly
  * over the 8 XCDs (all of a group's items on one XCD). A call that does not
- * walk launches one workgroup per item, longest query tiles first. A
- * walking call (16-bit inputs at head dim 64 or 128, items of at most 64 key
- * tiles on average) orders each XCD's items group by group, and launches
- * as many workgroups as the device holds at once (a multiple of 8), each
- * taking several items in rounds, when the items outnumber them. Any output
- * pointer may be NULL; `tiles` NULL queries only the sizes.
+ * walk launches one workgroup per item. A walking call (16-bit inputs at
+ * head dim 64 or 128, items of at most 64 key tiles on average) launches as
+ * many workgroups as the device holds at once (a multiple of 8), each
+ * taking several items in rounds, when the items outnumber them. Walking
+ * calls and unmasked 16-bit calls order each XCD's items group by group
+ * (each group's query tiles longest first); other calls put the longest
+ * query tiles first. Any output pointer may be NULL; `tiles` NULL queries
+ * only the sizes.
  * Returns FA355_OK or FA355_ERR_INVALID_ARG / FA355_ERR_UNSUPPORTED under
  * the same rules as mha_no_cache.
  */

@@ -122,8 +122,9 @@ def test_plan_covers_every_tile_once(shape):
     assert sorted(tiles) == sorted((t, b, h) for t in range(nq) for b in range(B)
                                    for h in range(0, H, hp))
     groups = B * Hkv
-    if pl["walk"] and groups % 8 == 0:
-        # Walk order: on each XCD (item w on XCD w % 8), group after group,
+    group_order = pl["walk"] or (mask == "none" and dt != fa.F32)
+    if group_order and groups % 8 == 0:
+        # Group order: on each XCD (item w on XCD w % 8), group after group,
         # each group's query tiles longest first.
         per_group = nq * (H // Hkv // hp)
         for x in range(8):

@@ -242,14 +242,24 @@ def test_growing_scores_raise_the_running_max(dt, mask, window):
     check(got, oracle.attention(q, kr, v, scale, mask, window), dt, f"growing scores {dt} {mask}")
 
 
-def test_huge_scale_one_hot():
-    """scale = 1e38 with small inputs: every |scale q.k| stays inside the
-    fp32 range, and the softmax is one-hot on each row's largest score."""
-    q, k, v = inputs.make_qkv(1, 300, 4, 2, 64, "f32", seed=22)
-    q, k = q * 0.02, k * 0.02
+@pytest.mark.parametrize("dt,D", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+def test_huge_scale_tiny_inputs(dt, D):
+    """scale = 1e38 on inputs of order 2^-60: q and k are small integers
+    times 2^-60, so every product is an exact, normal fp32 number and the
+    scores are exact multiples of 1e38 * 2^-120 (about 75), of order 1e3:
+    inside the supported |scale q.k| log2(e) < 2^24. The softmax is one-hot
+    on each row's largest score (shared between tied keys)."""
+    gen = torch.Generator().manual_seed(22)
+    B, S, H, Hkv = 1, 300, 4, 2
+    td = inputs.DTYPES[dt]
+    q = (torch.randint(-2, 3, (B, S, H, D), generator=gen).double() * 2.0 ** -60).to(td)
+    k = (torch.randint(-3, 4, (B, S, Hkv, D), generator=gen).double() * 2.0 ** -60).to(td)
+    v = torch.randn(B, S, Hkv, D, generator=gen).to(td)
+    sc = (q.double()[0, :, 0] @ k.double()[0, :, 0].T).abs().max() * 1e38
+    assert 1e2 < sc < 1e5, "scaled scores must be large but inside the supported range"
     got = run_gpu(q, k, v, 1e38, "causal", -1)
     want = oracle.attention(q, k, v, 1e38, "causal", -1)
-    check(got, want, "f32", "scale 1e38")
+    check(got, want, dt, f"scale 1e38 {dt} D{D}")
 
 
 def test_peaky_softmax_fp16_small():
