@@ -68,8 +68,6 @@ int heads_per_wg(int dtype, int D, int rep)
         if (hp <= waves_per_wg(dtype, D) && rep % hp == 0) return hp;
     return 1;
 }
-// Query rows per head in one workgroup (32 per wave).
-int block_m(int dtype, int D, int rep) { return 32 * waves_per_wg(dtype, D) / heads_per_wg(dtype, D, rep); }
 int block_n(int dtype, int D)
 {
     if (dtype == FA355_F32) return fa355::Tile32<64>::BN;
@@ -81,6 +79,38 @@ int block_n(int dtype, int D)
     }
 }
 
+// fp32 calls whose 32-row items number at most this many run the key-split
+// instance (mha_fwd32.hpp): one 32-row item per workgroup, its waves taking
+// every fourth key tile. Below one item per compute unit the call is bound
+// by each wave's serial MFMA chain, which the split shortens fourfold.
+constexpr int64_t kSplitMaxItems = 256;
+
+// How a call is decomposed: heads and rows per workgroup, key tile, items.
+struct Layout {
+    int hp;     // query heads per workgroup (sharing one K/V head)
+    int wph;    // waves per query head
+    int bm;     // query rows per head per workgroup
+    int bn;     // keys per tile
+    int split;  // fp32 key split
+    int64_t n_qtiles, n_items;
+};
+
+// D must be supported and H a multiple of Hkv.
+Layout layout_of(int B, int S, int H, int Hkv, int D, int dtype)
+{
+    Layout L;
+    const int rep = H / Hkv;
+    const int64_t items32 = ((int64_t)S + 31) / 32 * B * H;
+    L.split = dtype == FA355_F32 && fa355::split_dim32(D) && items32 <= kSplitMaxItems;
+    L.hp = L.split ? 1 : heads_per_wg(dtype, D, rep);
+    L.wph = L.split ? 1 : waves_per_wg(dtype, D) / L.hp;
+    L.bm = 32 * L.wph;
+    L.bn = block_n(dtype, D);
+    L.n_qtiles = ((int64_t)S + L.bm - 1) / L.bm;
+    L.n_items = L.n_qtiles * B * (H / L.hp);
+    return L;
+}
+
 // Shape checks shared by mha_no_cache and fa355_plan.
 int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
 {
@@ -89,9 +119,7 @@ int check_shape(int B, int S, int H, int Hkv, int D, int dtype)
     if (dtype != FA355_F32 && dtype != FA355_BF16 && dtype != FA355_F16)
         return FA355_ERR_INVALID_ARG;
     if (!supported_dim(D)) return FA355_ERR_UNSUPPORTED;
-    const int rep = H / Hkv;
-    const int64_t n_qtiles = ((int64_t)S + block_m(dtype, D, rep) - 1) / block_m(dtype, D, rep);
-    if (n_qtiles * B * (H / heads_per_wg(dtype, D, rep)) > INT32_MAX) return FA355_ERR_UNSUPPORTED;
+    if (layout_of(B, S, H, Hkv, D, dtype).n_items > INT32_MAX) return FA355_ERR_UNSUPPORTED;
     // Buffer offsets inside one tile are 32-bit: a tile spans at most 128
     // token rows of K/V and 32 of Q, so one token's row of q (H * D
     // elements) or of k / v (Hkv * D elements) may hold at most 16 MiB.
@@ -116,13 +144,10 @@ int clamped_window(int mask_kind, int window, int S)
     return mask_kind == FA355_MASK_SLIDING_WINDOW ? (window < S ? window : S) : S;
 }
 
-// Whether the call walks its work items (walk order; see fa355::walks).
-int call_walks(int dtype, int D, int rep, int mask_kind, int S, int window_clamped)
+// Whether the call walks its work items (see fa355::walks).
+int call_walks(int dtype, int D, const Layout &L, int mask_kind, int S, int window_clamped)
 {
-    return fa355::walks(dtype != FA355_F32, D, mask_kind, S, window_clamped, block_m(dtype, D, rep),
-                        block_n(dtype, D))
-               ? 1
-               : 0;
+    return fa355::walks(dtype != FA355_F32, D, mask_kind, S, window_clamped, L.bm, L.bn) ? 1 : 0;
 }
 
 // Whether the items are ordered group by group (see fa355::block_coord):
@@ -192,7 +217,7 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     rc = check_device();
     if (rc != FA355_OK) return rc;
 
-    Params p;
+    Params p{};
     p.out = out;
     p.q = q;
     p.k = k;
@@ -201,10 +226,12 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.S = S;
     p.H = H;
     p.Hkv = Hkv;
+    const Layout L = layout_of(B, S, H, Hkv, D, dtype);
     p.rep = H / Hkv;
-    p.hp = heads_per_wg(dtype, D, p.rep);
-    p.wph = waves_per_wg(dtype, D) / p.hp;
-    p.n_qtiles = (S + 32 * p.wph - 1) / (32 * p.wph);
+    p.hp = L.hp;
+    p.wph = L.wph;
+    p.kv_split = L.split;
+    p.n_qtiles = (int)L.n_qtiles;
     p.window = clamped_window(mask_kind, window, S);
     // exp(scale * s) = exp2(|scale| * log2(e) * (sign(scale) * s)); the sign
     // goes into Q (an exact bit flip) so the kernel's scale is never negative.
@@ -215,9 +242,8 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     const bool neg = std::signbit(scale) && scale != 0.0f;
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
 
-    const int grid = p.n_qtiles * B * (H / p.hp);
-    p.n_items = grid;
-    p.walk = call_walks(dtype, D, p.rep, mask_kind, S, p.window);
+    p.n_items = (int)L.n_items;
+    p.walk = call_walks(dtype, D, L, mask_kind, S, p.window);
     p.group_order = call_group_order(dtype, mask_kind, p.walk);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
@@ -274,13 +300,12 @@ extern "C" int fa355_plan(int B, int S, int H, int Hkv, int D, int dtype, int ma
     if (rc == FA355_ERR_INVALID_ARG) return rc;
     if (check_mask(mask_kind, window) != FA355_OK) return FA355_ERR_INVALID_ARG;
     if (rc != FA355_OK) return rc;
-    const int rep = H / Hkv, hp = heads_per_wg(dtype, D, rep), bm = block_m(dtype, D, rep);
-    const int n_qtiles = (S + bm - 1) / bm;
-    const int grid = n_qtiles * B * (H / hp);
-    const int walk = call_walks(dtype, D, rep, mask_kind, S, clamped_window(mask_kind, window, S));
+    const Layout L = layout_of(B, S, H, Hkv, D, dtype);
+    const int hp = L.hp, n_qtiles = (int)L.n_qtiles, grid = (int)L.n_items;
+    const int walk = call_walks(dtype, D, L, mask_kind, S, clamped_window(mask_kind, window, S));
     if (num_workgroups) *num_workgroups = grid;
-    if (block_m_out) *block_m_out = bm;
-    if (block_n_out) *block_n_out = block_n(dtype, D);
+    if (block_m_out) *block_m_out = L.bm;
+    if (block_n_out) *block_n_out = L.bn;
     if (heads_per_wg_out) *heads_per_wg_out = hp;
     if (walk_out) *walk_out = walk;
     if (tiles) {

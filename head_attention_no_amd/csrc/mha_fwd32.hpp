@@ -16,6 +16,14 @@
 //  * K and V go global -> registers -> LDS (double buffered); K rows are
 //    padded to an odd stride and V rows to D + 8 so the LDS reads of one
 //    wave hit distinct banks.
+//  * Key split (SPLIT, calls with few work items, head dim <= 64): a
+//    workgroup owns 32 query rows of one head, and its four waves take
+//    every fourth key tile each, each staging its own tiles in its own LDS
+//    block (no workgroup barrier in the key loop). At the end the four
+//    partial states (m, l, O) are merged exactly, as the online softmax
+//    merges tiles: O = sum_w 2^(m_w - M) O_w, l likewise, M = max_w m_w.
+//    This shortens the serial MFMA chain of each wave fourfold, which is
+//    what bounds a call with fewer workgroups than compute units.
 #pragma once
 
 #include "mha_common.hpp"
@@ -39,15 +47,22 @@ struct Tile32 {
     static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
 };
 
-template <int D, int MASK>
+// Head dims whose key-split instance is built (per-wave staging of a whole
+// tile takes D / 2 registers per lane, and four single-buffered tiles fit
+// in LDS).
+constexpr bool split_dim32(int D) { return D <= 64; }
+
+template <int D, int MASK, bool SPLIT>
 __global__ __launch_bounds__(kThreads32) __attribute__((amdgpu_waves_per_eu(Tile32<D>::WPE, Tile32<D>::WPE)))
 void mha_fwd32(Params p)
 {
     using TL = Tile32<D>;
     constexpr int BN = TL::BN;
     constexpr int ND = TL::ND;
+    static_assert(!SPLIT || split_dim32(D), "key split is built for head dims up to 64");
 
-    __shared__ __attribute__((aligned(16))) float lds[2 * TL::STAGE];
+    // Normal: two stages shared by the workgroup. Key split: one stage per wave.
+    __shared__ __attribute__((aligned(16))) float lds[(SPLIT ? kWaves32 : 2) * TL::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -57,11 +72,11 @@ void mha_fwd32(Params p)
 
     const TileCoord tc = block_coord(blockIdx.x, p.n_qtiles, p.B, p.H, p.Hkv, p.hp, 0);
     const int b = tc.b, kvh = tc.h / p.rep;
-    const int h = tc.h + wave / p.wph;  // this wave's query head
-    const int rows = 32 * p.wph;        // query rows per head in this workgroup
+    const int h = SPLIT ? tc.h : tc.h + wave / p.wph;  // this wave's query head
+    const int rows = SPLIT ? 32 : 32 * p.wph;         // query rows per head in this workgroup
     const int S = p.S, W = p.window;
     const int q0 = tc.qt * rows;
-    const int wrow0 = q0 + (wave % p.wph) * 32;
+    const int wrow0 = SPLIT ? q0 : q0 + (wave % p.wph) * 32;
     const int row = wrow0 + c32;  // this lane's query row
 
     const float *__restrict__ Q = static_cast<const float *>(p.q);
@@ -90,14 +105,18 @@ void mha_fwd32(Params p)
     int kt_begin, kt_end;
     key_tile_range<MASK, BN>(q0, rows, S, W, kt_begin, kt_end);
 
-    // Staging: every thread moves D/32 rows x 16 bytes of K and of V.
+    // Staging: every thread moves D/32 rows x 16 bytes of K and of V (key
+    // split: each wave moves its own tiles, D/8 rows per lane).
+    constexpr int STAGERS = SPLIT ? 64 : kThreads32;
+    const int sid = SPLIT ? lane : tid;
+    float *const stage0 = lds + (SPLIT ? wave * TL::STAGE : 0);
     constexpr int CPR = D / 4;
-    constexpr int STEP = kThreads32 / CPR;
+    constexpr int STEP = STAGERS / CPR;
     constexpr int R = BN / STEP;
     u32x4 stg[2 * R];
     auto load_tile = [&](int kt) {
         const int k0 = kt * BN;
-        const int c = tid % CPR, kr = tid / CPR;
+        const int c = sid % CPR, kr = sid / CPR;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int key = min(k0 + kr + r * STEP, S - 1);  // rows past S are masked
@@ -106,9 +125,9 @@ void mha_fwd32(Params p)
         }
     };
     auto store_tile = [&](int buf) {
-        float *Ks = lds + buf * TL::STAGE;
+        float *Ks = stage0 + buf * TL::STAGE;
         float *Vs = Ks + TL::K_ELEMS;
-        const int c = tid % CPR, kr = tid / CPR;
+        const int c = sid % CPR, kr = sid / CPR;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int key = kr + r * STEP;
@@ -126,20 +145,27 @@ void mha_fwd32(Params p)
     float l_run = 0.0f;       // this lane's share of the running sum
     const float sl2e = p.scale_log2;
 
-    load_tile(kt_begin);
-    store_tile(0);
-    __syncthreads();
+    // Key tiles of this wave: all of the workgroup's, or (key split) every
+    // fourth one from kt_begin + wave.
+    const int kt_first = SPLIT ? kt_begin + wave : kt_begin;
+    constexpr int KT_STEP = SPLIT ? kWaves32 : 1;
 
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int buf = (kt - kt_begin) & 1;
-        const bool has_next = kt + 1 < kt_end;
-        if (has_next) load_tile(kt + 1);
+    if (kt_first < kt_end) {
+        load_tile(kt_first);
+        store_tile(0);
+    }
+    if (!SPLIT) __syncthreads();
+
+    for (int kt = kt_first; kt < kt_end; kt += KT_STEP) {
+        const int buf = SPLIT ? 0 : (kt - kt_begin) & 1;
+        const bool has_next = kt + KT_STEP < kt_end;
+        if (has_next) load_tile(kt + KT_STEP);
 
         const int k0 = kt * BN;
         const int cls = classify<MASK>(wrow0, k0, k0 + BN - 1, S, W);
         auto tile_body = [&](auto edge_tag) {
             constexpr bool EDGE = decltype(edge_tag)::value;
-            const float *Kf = lds + buf * TL::STAGE;
+            const float *Kf = stage0 + buf * TL::STAGE;
             const float *Vf = Kf + TL::K_ELEMS;
 
             f32x16 sacc = f32x16{};
@@ -191,8 +217,56 @@ void mha_fwd32(Params p)
         if (cls == kFull) tile_body(std::false_type{});
         else if (cls == kEdge) tile_body(std::true_type{});
 
-        if (has_next) store_tile(buf ^ 1);
+        if constexpr (SPLIT) {
+            // The wave's own block: its reads of this tile are issued before
+            // the writes of the next one, and LDS executes a wave's
+            // operations in order.
+            if (has_next) store_tile(0);
+        } else {
+            if (has_next) store_tile(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    if constexpr (SPLIT) {
+        // Merge the four waves' (m, l, O): waves 1-3 publish theirs through
+        // LDS (same lane layout), wave 0 combines and stores.
+        __syncthreads();  // every wave is done with its staging block
+        constexpr int PART = 2 + 16 * ND;  // floats per lane
+        if (wave > 0) {
+            float *part = lds + (wave - 1) * PART * 64;
+            part[lane] = m_run;
+            part[64 + lane] = l_run;
+#pragma unroll
+            for (int t = 0; t < ND; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[(2 + 16 * t + r) * 64 + lane] = oacc[t][r];
+        }
         __syncthreads();
+        if (wave > 0) return;
+        float mw[kWaves32];
+        mw[0] = m_run;
+        float mx = m_run;
+#pragma unroll
+        for (int w = 1; w < kWaves32; ++w) {
+            mw[w] = lds[(w - 1) * PART * 64 + lane];
+            mx = fmaxf(mx, mw[w]);
+        }
+        float f[kWaves32];
+#pragma unroll
+        for (int w = 0; w < kWaves32; ++w) f[w] = mw[w] == -INFINITY ? 0.0f : exp2_fast(mw[w] - mx);
+        l_run *= f[0];
+#pragma unroll
+        for (int t = 0; t < ND; ++t) oacc[t] *= f[0];
+#pragma unroll
+        for (int w = 1; w < kWaves32; ++w) {
+            const float *pw = lds + (w - 1) * PART * 64;
+            l_run += f[w] * pw[64 + lane];
+#pragma unroll
+            for (int t = 0; t < ND; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[t][r] += f[w] * pw[(2 + 16 * t + r) * 64 + lane];
+        }
     }
 
     const float inv = 1.0f / half_sum(l_run);

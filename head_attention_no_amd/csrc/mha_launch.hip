@@ -44,7 +44,12 @@ hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
 {
     void *args[] = {const_cast<Params *>(&p)};
     if constexpr (std::is_same_v<T, float>) {
-        return hipLaunchKernel(reinterpret_cast<const void *>(&mha_fwd32<D, MASK>), dim3(n_items),
+        if constexpr (split_dim32(D)) {
+            if (p.kv_split)
+                return hipLaunchKernel(reinterpret_cast<const void *>(&mha_fwd32<D, MASK, true>),
+                                       dim3(n_items), dim3(kThreads32), args, 0, stream);
+        }
+        return hipLaunchKernel(reinterpret_cast<const void *>(&mha_fwd32<D, MASK, false>), dim3(n_items),
                                dim3(kThreads32), args, 0, stream);
     } else {
         const void *kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK>);

@@ -132,7 +132,10 @@ const char *fa355_version(void);
  * and window are those of the call. A work item computes the same block_m
  * query rows of heads_per_wg consecutive query heads, which share one K/V
  * head (heads_per_wg is the largest of 8, 4, 2, 1 that divides H / Hkv and
- * fits the kernel's waves), against key tiles of block_n keys. Reports the
+ * fits the kernel's waves), against key tiles of block_n keys. fp32 calls
+ * at head dim 32 or 64 whose 32-row items number at most 256 use items of
+ * 32 rows of one head, the workgroup's four waves each taking every fourth
+ * key tile and merging their partial softmax states exactly at the end. Reports the
  * number of work items (num_workgroups), whether the call walks them
  * (walk: 0 or 1) and, for each of the first `n` item indices, what it
  * computes: tiles[3*w + 0] = query tile (rows tile*block_m ...
