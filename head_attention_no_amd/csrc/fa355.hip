@@ -241,6 +241,10 @@ extern "C" int mha_no_cache(void *out, const void *q, const void *k, const void 
     p.scale_log2 = (float)std::fmax(std::fabs((double)scale) * kLog2e, 1e-30);
     const bool neg = std::signbit(scale) && scale != 0.0f;
     p.q_sign = neg ? (dtype == FA355_F32 ? 0x80000000u : 0x80008000u) : 0u;
+    // Pre-scaled Q at head dims 32 and 64 (mha_fwd16.hpp), unless the scaled
+    // fp16 values could overflow: |q * scale * log2(e)| <= |q| needs
+    // |scale| log2(e) <= 1.
+    p.prescale = dtype != FA355_F32 && D <= 64 && (dtype == FA355_BF16 || p.scale_log2 <= 1.0f);
 
     p.n_items = (int)L.n_items;
     p.walk = call_walks(dtype, D, L, mask_kind, S, p.window);

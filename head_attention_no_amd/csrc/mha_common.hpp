@@ -42,6 +42,7 @@ struct Params {
     int walk;      // 1: a grid below n_items makes each workgroup walk several items
     int group_order;  // 1: items in group order (see block_coord)
     int kv_split;  // 1: fp32 key split (mha_fwd32.hpp): 32-row items, keys split over the waves
+    int prescale;  // 1: 16-bit kernel with Q pre-scaled by scale_log2 (mha_fwd16.hpp, D <= 64)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|

@@ -52,7 +52,10 @@ hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
         return hipLaunchKernel(reinterpret_cast<const void *>(&mha_fwd32<D, MASK, false>), dim3(n_items),
                                dim3(kThreads32), args, 0, stream);
     } else {
-        const void *kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK>);
+        const void *kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK, false>);
+        if constexpr (Tile16<D>::PRESCALE) {
+            if (p.prescale) kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK, true>);
+        }
         constexpr int threads = 64 * Tile16<D>::NW;
         int grid = n_items;
         // A walking call (p.walk, set by the C-ABI layer for short items at
@@ -61,8 +64,8 @@ hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
         // workgroup then walks several items.
         if constexpr (Tile16<D>::WALK) {
             if (p.walk) {
-                static std::atomic<int> cache[kMaxDevices];
-                const int slots = resident_workgroups(kernel, threads, cache) / 8 * 8;
+                static std::atomic<int> cache[2][kMaxDevices];  // per kernel variant
+                const int slots = resident_workgroups(kernel, threads, cache[p.prescale ? 1 : 0]) / 8 * 8;
                 if (slots > 0 && slots < n_items) grid = slots;
             }
         }
