@@ -32,6 +32,24 @@ constexpr int kTopkMaxK = 1024;
 constexpr int kTopkUnroll = 4;  // float4 loads in flight per thread and chunk
 constexpr int kTopkCand = 4096;  // LDS room for the entries of the threshold bin
 constexpr int kTopkChunkVec = 2048;  // float4 vectors in the first chunk (8192 entries)
+constexpr int kTopkSmallK = 64;      // the wave-sort path: K up to one wave's lanes
+constexpr int kTopkBatchVec = kTopkThreads * kTopkUnroll;  // float4 vectors per batch (16384 entries)
+constexpr int kTopkListCap = 320;    // candidate slots per wave on the wave-sort path
+
+// LDS beside the 4096-bin histogram: either the selection and candidate
+// arrays of the paths that read the row twice, or the wave-sort path's 16
+// candidate lists.
+union TopkLds {
+    struct {
+        uint32_t sel_key[kTopkMaxK];
+        int32_t sel_idx[kTopkMaxK];
+        uint32_t cand_key[kTopkCand];
+        int32_t cand_idx[kTopkCand];
+    } g;
+    uint64_t lists[kTopkThreads / 64][kTopkListCap];
+};
+static_assert(sizeof(uint64_t[kTopkThreads / 64][kTopkListCap]) <= 2 * kTopkMaxK * 4 + 2 * kTopkCand * 4,
+              "the lists share the selection arrays' space");
 
 struct TopkParams {
     float *values;
@@ -47,6 +65,109 @@ __device__ inline uint32_t order_key(float f)
     uint32_t u = __float_as_uint(f);
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-sort path entries: 64-bit words whose unsigned order is the result
+// order. High word: the order key; low word: (0x7FFFFFFF - index) << 1,
+// larger for lower indices, with bit 0 set for -0.0 (so the value comes
+// back bit for bit). 0 sorts after every entry and pads.
+__device__ inline uint64_t entry_word(uint32_t bits, int idx)
+{
+    return ((uint64_t)order_key(__uint_as_float(bits)) << 32) |
+           ((uint32_t)(0x7FFFFFFF - idx) << 1) | (uint32_t)(bits == 0x80000000u);
+}
+
+__device__ inline int entry_index(uint64_t w) { return 0x7FFFFFFF - (int)((uint32_t)w >> 1); }
+
+__device__ inline float entry_value(uint64_t w)
+{
+    const uint32_t key = (uint32_t)(w >> 32);
+    uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+    if (w & 1u) u = 0x80000000u;
+    return __uint_as_float(u);
+}
+
+// The value of lane (lane ^ STRIDE), on the vector ALU only. DPP inside
+// 16-lane rows: quad permutes for 1 and 2; row rotations for 4 (lane i
+// reads lane i - n, n = 4 or 12, by bit 2 of the lane) and 8 (symmetric).
+// Across rows: v_permlane16_swap / v_permlane32_swap with the value as
+// both operands; the first result then holds, in the upper row (half) of
+// each pair, the lower one's values, the second result the converse.
+template <int STRIDE>
+__device__ inline uint32_t lane_xor(uint32_t v)
+{
+    const int lane = threadIdx.x & 63;
+    if constexpr (STRIDE == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (STRIDE == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (STRIDE == 4) {
+        const uint32_t down = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, false);    // row_ror:12
+        return (lane & 4) ? down : up;
+    } else if constexpr (STRIDE == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (STRIDE == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? s[0] : s[1];
+    } else {
+        const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? s[0] : s[1];
+    }
+}
+
+// One compare-exchange of a bitonic network held in a wave, one 64-bit
+// entry per lane (as two words): the lane keeps the larger or the smaller
+// of its entry and its partner's.
+template <int STRIDE>
+__device__ inline void wave_cx(uint32_t &hi, uint32_t &lo, bool keep_larger)
+{
+    const uint32_t ph = lane_xor<STRIDE>(hi), pl = lane_xor<STRIDE>(lo);
+    const uint64_t a = ((uint64_t)hi << 32) | lo, b = ((uint64_t)ph << 32) | pl;
+    // Equal entries (padding only) may swap: harmless. Selects, no branches.
+    const bool take = (b > a) == keep_larger;
+    hi = take ? ph : hi;
+    lo = take ? pl : lo;
+}
+
+// Bitonic merge: a bitonic sequence over the wave's 64 lanes, sorted
+// descending (lane 0 largest).
+template <int STRIDE>
+__device__ inline void wave_merge_desc(uint32_t &hi, uint32_t &lo)
+{
+    wave_cx<STRIDE>(hi, lo, ((threadIdx.x & 63) & STRIDE) == 0);
+    if constexpr (STRIDE > 1) wave_merge_desc<STRIDE / 2>(hi, lo);
+}
+
+// Bitonic sort of the wave's 64 entries, descending: blocks of SIZE
+// alternate direction until the last, which runs descending.
+template <int SIZE, int STRIDE>
+__device__ inline void wave_sort_stage(uint32_t &hi, uint32_t &lo)
+{
+    const int lane = threadIdx.x & 63;
+    const bool desc = SIZE == 64 || (lane & SIZE) == 0;
+    wave_cx<STRIDE>(hi, lo, ((lane & STRIDE) == 0) == desc);
+    if constexpr (STRIDE > 1) wave_sort_stage<SIZE, STRIDE / 2>(hi, lo);
+}
+
+template <int SIZE = 2>
+__device__ inline void wave_sort_desc(uint32_t &hi, uint32_t &lo)
+{
+    wave_sort_stage<SIZE, SIZE / 2>(hi, lo);
+    if constexpr (SIZE < 64) wave_sort_desc<SIZE * 2>(hi, lo);
+}
+
+// Both lists sorted descending; afterwards (hi, lo) holds the 64 largest
+// of the two, sorted descending. (rh, rl) is the other list read in
+// reverse lane order: the lane-wise larger of a descending and an
+// ascending list is a bitonic sequence holding the top half.
+__device__ inline void wave_keep_top(uint32_t &hi, uint32_t &lo, uint32_t rh, uint32_t rl)
+{
+    const uint64_t a = ((uint64_t)hi << 32) | lo, b = ((uint64_t)rh << 32) | rl;
+    const bool take = b > a;
+    hi = take ? rh : hi;
+    lo = take ? rl : lo;
+    wave_merge_desc<32>(hi, lo);
 }
 
 // Exclusive prefix sum of v over the workgroup in thread order; `total`
@@ -135,12 +256,11 @@ __device__ inline void lds_bitonic_sort(uint32_t *key, int32_t *idx, int n)
 
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
 {
-    __shared__ uint32_t hist[4096];
-    __shared__ uint32_t sel_key[kTopkMaxK];
-    __shared__ int32_t sel_idx[kTopkMaxK];
-    __shared__ uint32_t cand_key[kTopkCand];
-    __shared__ int32_t cand_idx[kTopkCand];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
+    __shared__ TopkLds lds;
     __shared__ int n_cand, n_tie;
+    __shared__ int list_len[kTopkThreads / 64];
+    __shared__ uint32_t top_key;
     __shared__ int scratch[kTopkThreads / 64];
     __shared__ int found[2];  // bin, entries still needed within it
     __shared__ int n_greater;
@@ -236,7 +356,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     // digit still ties, the lowest indices of the tied entries.
     auto pick = [&](int nc, int base, int want) {
         auto visit_cand = [&](auto &&fn) {
-            for (int i = tid; i < nc; i += kTopkThreads) fn(cand_key[i], (int)cand_idx[i]);
+            for (int i = tid; i < nc; i += kTopkThreads) fn(lds.g.cand_key[i], (int)lds.g.cand_idx[i]);
         };
         prefix = 0u;
         mask = 0u;
@@ -259,15 +379,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
             if (k > prefix) {
                 const int s = atomicAdd(&n_greater, 1);  // < gt by the select invariant
                 if (s < gt) {
-                    sel_key[base + s] = key;
-                    sel_idx[base + s] = idx;
+                    lds.g.sel_key[base + s] = key;
+                    lds.g.sel_idx[base + s] = idx;
                 }
             } else if (k == prefix) {
                 const int s = atomicAdd(&n_tie, 1);  // < last
                 if (!by_index) {
                     if (s < need) {
-                        sel_key[base + gt + s] = key;
-                        sel_idx[base + gt + s] = idx;
+                        lds.g.sel_key[base + gt + s] = key;
+                        lds.g.sel_idx[base + gt + s] = idx;
                     }
                 } else if (s < kTopkCand) {
                     tie[s] = idx;
@@ -279,14 +399,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
             int tp = 1;
             while (tp < last) tp <<= 1;
             for (int i = tid; i < tp; i += kTopkThreads) {
-                cand_key[i] = 0u;  // equal keys: the sort orders by index
-                cand_idx[i] = i < last ? tie[i] : 0x7fffffff;
+                lds.g.cand_key[i] = 0u;  // equal keys: the sort orders by index
+                lds.g.cand_idx[i] = i < last ? tie[i] : 0x7fffffff;
             }
             __syncthreads();
-            lds_bitonic_sort(cand_key, cand_idx, tp);
+            lds_bitonic_sort(lds.g.cand_key, lds.g.cand_idx, tp);
             for (int i = tid; i < need; i += kTopkThreads) {
-                sel_key[base + gt + i] = prefix;
-                sel_idx[base + gt + i] = cand_idx[i];
+                lds.g.sel_key[base + gt + i] = prefix;
+                lds.g.sel_idx[base + gt + i] = lds.g.cand_idx[i];
             }
             __syncthreads();
         }
@@ -301,8 +421,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
             if ((key & mask) > prefix) {
                 const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
                 if (s < greater) {
-                    sel_key[s] = key;
-                    sel_idx[s] = idx;
+                    lds.g.sel_key[s] = key;
+                    lds.g.sel_idx[s] = idx;
                 }
             }
         };
@@ -319,8 +439,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
                 for (int e = 0; e < cnt; ++e)
                     if ((key[e] & mask) == prefix) {
                         if (rank < need) {
-                            sel_key[greater + rank] = key[e];
-                            sel_idx[greater + rank] = idx0 + e;
+                            lds.g.sel_key[greater + rank] = key[e];
+                            lds.g.sel_idx[greater + rank] = idx0 + e;
                         }
                         ++rank;
                     }
@@ -355,6 +475,190 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         __syncthreads();
     };
 
+    // Wave-sort path (K <= 64, rows of 49152 entries or more), one read.
+    // The row streams in batches of 16384 entries (4 float4 per thread),
+    // four batches in flight. Once the first four are in, each thread's
+    // largest of its 64 entries gives 1024 distinct entries; the bin of
+    // their K-th largest key (4096-bin histogram of the top 12 key bits,
+    // searched downward from the top one by one wave) bounds the row's K-th
+    // largest from below. Each wave appends the entries at or above the
+    // bound that it reads to a list of its own in LDS (ballot compaction,
+    // no atomics). The lists, joined, are cut into chunks of 64 that waves
+    // sort in registers, and a tree of bitonic merges between waves leaves
+    // the row's 64 largest, in order, in wave 0. A list that would overflow
+    // sends the row to the paths below.
+    if (K <= kTopkSmallK && nvec >= 4 * kTopkBatchVec) {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int nb = (nvec + kTopkBatchVec - 1) / kTopkBatchVec;
+        // Loads past the row's end read its last vector again (results unused).
+        auto load = [&](int b, float4 (&d)[kTopkUnroll]) {
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) d[u] = xv[min(b * kTopkBatchVec + u * kTopkThreads + tid, nvec - 1)];
+        };
+        float4 r0[kTopkUnroll], r1[kTopkUnroll], r2[kTopkUnroll], r3[kTopkUnroll];
+        load(0, r0);
+        load(1, r1);
+        load(2, r2);
+        load(3, r3);
+        for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
+        if (tid == 0) top_key = 0u;
+        __syncthreads();
+        {
+            // Largest of the thread's 64 entries (all inside the row), as a key.
+            float mx = -INFINITY;
+            auto fold = [&](const float4 (&d)[kTopkUnroll]) {
+#pragma unroll
+                for (int u = 0; u < kTopkUnroll; ++u) mx = fmaxf(fmaxf(mx, fmaxf(d[u].x, d[u].y)), fmaxf(d[u].z, d[u].w));
+            };
+            fold(r0);
+            fold(r1);
+            fold(r2);
+            fold(r3);
+            const uint32_t key = order_key(mx);
+            atomicAdd(&hist[key >> 20], 1u);
+            uint32_t wmax = key;
+            wmax = max(wmax, lane_xor<1>(wmax));
+            wmax = max(wmax, lane_xor<2>(wmax));
+            wmax = max(wmax, lane_xor<4>(wmax));
+            wmax = max(wmax, lane_xor<8>(wmax));
+            wmax = max(wmax, lane_xor<16>(wmax));
+            wmax = max(wmax, lane_xor<32>(wmax));
+            if (lane == 0) atomicMax(&top_key, wmax);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // Bins from the top one down, 64 at a time (lane l: bin top - l):
+            // the first bin where the count from the top reaches K. The
+            // 1024 counted keys guarantee one.
+            int top = (int)(top_key >> 20), above = 0, bin = 0;
+            for (; top >= 0; top -= 64) {
+                const int c = top - lane >= 0 ? (int)hist[top - lane] : 0;
+                int s = c;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int y = __shfl_up(s, d, 64);
+                    if (lane >= d) s += y;
+                }
+                const uint64_t m = __builtin_amdgcn_ballot_w64(above + s >= K);
+                if (m) {
+                    bin = top - __builtin_ctzll(m);
+                    break;
+                }
+                above += __shfl(s, 63, 64);
+            }
+            if (lane == 0) found[0] = bin;
+        }
+        __syncthreads();
+        // No entry has key 0x7FFFFFFF (-0.0 maps to +0.0's key): lowering a
+        // bound of 0x80000000 by one admits nothing more.
+        const uint32_t lo = ((uint32_t)found[0] << 20) - (found[0] == 2048 ? 1u : 0u);
+        // key >= lo as one compare of the raw bits u: for a positive bound,
+        // (int)u >= (int)(lo & 0x7FFFFFFF); else u <= ~lo (unsigned).
+        const bool positive = lo > 0x80000000u;
+        const int lo_bits = (int)(lo & 0x7FFFFFFFu);
+        const uint32_t not_lo = ~lo;
+        int cnt = 0;  // wave-uniform; above kTopkListCap the list has overflowed
+        auto append = [&](bool cand, uint32_t bits, int idx) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+            if (m) {
+                const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (cand && pos < kTopkListCap) lds.lists[wave][pos] = entry_word(bits, idx);
+                cnt += __builtin_popcountll(m);
+            }
+        };
+        auto process_as = [&](auto pos, int b, const float4 (&d)[kTopkUnroll]) {
+#pragma unroll
+            for (int u = 0; u < kTopkUnroll; ++u) {
+                const int j = b * kTopkBatchVec + u * kTopkThreads + tid;
+                const bool valid = j < nvec;
+                const int e = head + 4 * j;
+                const uint32_t w[4] = {__float_as_uint(d[u].x), __float_as_uint(d[u].y),
+                                       __float_as_uint(d[u].z), __float_as_uint(d[u].w)};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool above = decltype(pos)::value ? (int)w[c] >= lo_bits : w[c] <= not_lo;
+                    append(valid && above, w[c], e + c);
+                }
+            }
+        };
+        auto process = [&](int b, const float4 (&d)[kTopkUnroll]) {
+            if (positive)
+                process_as(std::true_type{}, b, d);
+            else
+                process_as(std::false_type{}, b, d);
+        };
+        for (int b = 0; b < nb; b += 4) {
+            process(b, r0);
+            load(b + 4, r0);
+            if (b + 1 < nb) process(b + 1, r1);
+            load(b + 5, r1);
+            if (b + 2 < nb) process(b + 2, r2);
+            load(b + 6, r2);
+            if (b + 3 < nb) process(b + 3, r3);
+            load(b + 7, r3);
+        }
+        {
+            const float h = tid < head ? x[tid] : 0.f;
+            append(tid < head && order_key(h) >= lo, __float_as_uint(h), tid);
+            const float t = tail0 + tid < V ? x[tail0 + tid] : 0.f;
+            append(tail0 + tid < V && order_key(t) >= lo, __float_as_uint(t), tail0 + tid);
+        }
+        if (lane == 0) list_len[wave] = cnt;
+        __syncthreads();
+        int total = 0;
+        bool overflowed = false;
+#pragma unroll
+        for (int w = 0; w < kTopkThreads / 64; ++w) {
+            total += list_len[w];
+            overflowed |= list_len[w] > kTopkListCap;
+        }
+        if (!overflowed) {
+            // The lists, end to end, cut into chunks of 64; wave w sorts
+            // chunks w, w + 16, .. and keeps the 64 largest, descending (0 pads).
+            const int nchunks = (total + 63) >> 6;
+            uint32_t th = 0u, tl = 0u;
+            for (int c = wave; c < nchunks; c += kTopkThreads / 64) {
+                const int g = 64 * c + lane;  // position in the joined lists
+                int src = 0, base = 0;        // slot in lds.lists of position g
+#pragma unroll
+                for (int w = 0; w < kTopkThreads / 64; ++w) {
+                    const int n = list_len[w];
+                    if (g >= base && g < base + n) src = w * kTopkListCap + g - base;
+                    base += n;
+                }
+                const uint64_t v = g < total ? (&lds.lists[0][0])[src] : 0ull;
+                uint32_t h = (uint32_t)(v >> 32), l = (uint32_t)v;
+                wave_sort_desc(h, l);
+                if (c == wave) {
+                    th = h;
+                    tl = l;
+                } else {
+                    wave_keep_top(th, tl, (uint32_t)__shfl((int)h, 63 - lane, 64), (uint32_t)__shfl((int)l, 63 - lane, 64));
+                }
+            }
+            // Tree of merges over the waves that hold a list: at level s,
+            // wave w + s hands its list to wave w (w a multiple of 2s)
+            // through LDS (the histogram's space).
+            const int nlists = min(nchunks, kTopkThreads / 64);
+            uint64_t *const xbuf = reinterpret_cast<uint64_t *>(hist);
+            for (int s = 1; s < nlists; s <<= 1) {
+                if ((wave & (2 * s - 1)) == s && wave < nlists) xbuf[wave * 64 + lane] = ((uint64_t)th << 32) | tl;
+                __syncthreads();
+                if ((wave & (2 * s - 1)) == 0 && wave + s < nlists) {
+                    const uint64_t o = xbuf[(wave + s) * 64 + 63 - lane];
+                    wave_keep_top(th, tl, (uint32_t)(o >> 32), (uint32_t)o);
+                }
+            }
+            if (wave == 0 && lane < K) {
+                const uint64_t wd = ((uint64_t)th << 32) | tl;
+                p.values[(int64_t)blockIdx.x * K + lane] = entry_value(wd);
+                p.indices[(int64_t)blockIdx.x * K + lane] = entry_index(wd);
+            }
+            return;
+        }
+    }
+
     bool done = false;
     // Single-read path for rows longer than 16384 entries. The bin of the
     // K-th largest entry of the first chunk (8192 entries) bounds the row's
@@ -384,8 +688,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
             if (key >= lo) {
                 const int s = atomicAdd(&n_cand, 1);
                 if (s < kTopkCand) {
-                    cand_key[s] = key;
-                    cand_idx[s] = idx;
+                    lds.g.cand_key[s] = key;
+                    lds.g.cand_idx[s] = idx;
                 }
             }
         });
@@ -417,14 +721,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
                 if (k > prefix) {
                     const int s = atomicAdd(&n_greater, 1);  // < greater by the select invariant
                     if (s < greater) {
-                        sel_key[s] = key;
-                        sel_idx[s] = idx;
+                        lds.g.sel_key[s] = key;
+                        lds.g.sel_idx[s] = idx;
                     }
                 } else if (k == prefix) {
                     const int s = atomicAdd(&n_cand, 1);  // < in_bin
                     if (s < kTopkCand) {
-                        cand_key[s] = key;
-                        cand_idx[s] = idx;
+                        lds.g.cand_key[s] = key;
+                        lds.g.cand_idx[s] = idx;
                     }
                 }
             });
@@ -441,14 +745,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     int kp = 1;
     while (kp < K) kp <<= 1;
     if (tid >= K && tid < kp) {
-        sel_key[tid] = 0u;
-        sel_idx[tid] = 0x7fffffff;
+        lds.g.sel_key[tid] = 0u;
+        lds.g.sel_idx[tid] = 0x7fffffff;
     }
     __syncthreads();
-    lds_bitonic_sort(sel_key, sel_idx, kp);
+    lds_bitonic_sort(lds.g.sel_key, lds.g.sel_idx, kp);
 
     if (tid < K) {
-        const int idx = sel_idx[tid];
+        const int idx = lds.g.sel_idx[tid];
         p.values[(int64_t)blockIdx.x * K + tid] = x[idx];
         p.indices[(int64_t)blockIdx.x * K + tid] = idx;
     }

@@ -48,6 +48,14 @@ CASES = [
     # threshold bins of more than 4096 entries: the multi-pass path
     (2, 20000, 100, "zeros"),
     (2, 50000, 300, "ties"),
+    # K <= 64 on rows of 49152 entries or more: the wave-sort path (rows
+    # start at every 16-byte phase), and its hand-over to the paths above
+    # when a wave's candidate list overflows (ties, zeros)
+    (3, 100003, 64, "normal"),
+    (4, 49157, 1, "normal"),
+    (2, 131071, 33, "frequencies"),
+    (2, 49153, 33, "zeros"),
+    (2, 98304, 64, "huge_tiny"),
 ]
 
 
@@ -57,6 +65,32 @@ def test_topk_matches_oracle(case):
     note(f"topk case {case}")
     x = inputs.make_scores(B, V, kind, seed=V + k)
     check(x, k)
+
+
+def test_topk_negative_rows():
+    """All-negative rows: the wave-sort path's bound is a negative value."""
+    x = inputs.make_scores(3, 70001, "normal", seed=11) - 10.0
+    check(x, 50)
+
+
+def test_topk_zeros_among_negatives():
+    """A thousand signed zeros among negatives, K = 64: the K-th largest
+    is zero, every chosen value ties at zero and the lowest indices win;
+    -0.0 comes back bit for bit."""
+    g = torch.Generator("cpu").manual_seed(5)
+    x = -(inputs.make_scores(2, 90000, "normal", seed=12).abs() + 1.0)
+    for r in range(2):
+        pos = torch.randperm(90000, generator=g)[:1000]
+        sign = torch.randint(0, 2, (1000,), generator=g).to(torch.bool)
+        x[r, pos] = torch.where(sign, torch.tensor(-0.0), torch.tensor(0.0))
+    check(x, 64)
+
+
+def test_topk_ascending_rows():
+    """Increasing rows: the first batch bounds nothing away, so a wave's
+    list overflows and the row goes to the two-read paths."""
+    x = torch.arange(2 * 60000, dtype=torch.float32).view(2, 60000) / 7.0
+    check(x, 20)
 
 
 def test_topk_full_size_workload():
