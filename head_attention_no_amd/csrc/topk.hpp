@@ -6,21 +6,33 @@
 // values by ascending index (-0.0 equals +0.0), as values and indices.
 //
 // One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
-// order keys (larger float, larger key). Long rows first try one read: a
-// histogram of the first 8192 entries bounds the K-th largest key from below, and
-// the one read keeps every entry above the bound as a candidate in LDS
-// (sorted there) unless there are more than 4096. Otherwise a
-// histogram of the top 12 key bits (in LDS) finds the bin of the K-th
-// largest entry of the row. Usually that bin holds
-// few entries: a second and last read of the row then collects the entries
-// of higher bins and those of the bin itself (candidates, at most 4096)
-// into LDS, where a bitonic sort of the candidates by (key descending,
-// index ascending) picks the ones still needed. When the bin is larger, the
-// radix select continues over the next 12 and 8 bits (stopping once every
-// entry sharing the prefix is wanted), and a gather pass takes the entries
-// above the prefix and the tied entries in index order (block-wide prefix
-// counts over each chunk of the row). Either way a last bitonic sort of the
-// K chosen (key, index) pairs orders them.
+// order keys (larger float, larger key).
+//
+// K <= 64 on long rows (the sampler's case): one read. Four batches of
+// 16384 entries stream in; each thread's largest entry bounds the row's
+// K-th largest from below (their K-th largest, found with a histogram of
+// the top 12 key bits), and the rest of the row streams while every entry
+// at or above the bound joins a candidate list in LDS. Up to 256
+// candidates are ranked by counting (all waves share the comparisons);
+// more are sorted in 64-entry chunks in registers (bitonic network over
+// DPP and permlane exchanges) and merged by a tree of bitonic merges. A
+// list of more than 5120 candidates (heavily tied rows) sends the row to
+// the paths below.
+//
+// Otherwise, long rows first try one read: a histogram of the first 8192
+// entries bounds the K-th largest key from below, and the one read keeps
+// every entry above the bound as a candidate in LDS unless there are more
+// than 4096. Otherwise a histogram of the top 12 key bits (in LDS) finds
+// the bin of the K-th largest entry of the row. Usually that bin holds few
+// entries: a second and last read of the row then collects the entries of
+// higher bins and those of the bin itself (candidates, at most 4096) into
+// LDS, where a radix select over the candidates picks the ones still
+// needed. When the bin is larger, the radix select continues over the
+// next 12 and 8 bits (stopping once every entry sharing the prefix is
+// wanted), and a gather pass takes the entries above the prefix and the
+// tied entries in index order (block-wide prefix counts over each chunk of
+// the row). Either way a last bitonic sort of the K chosen (key, index)
+// pairs orders them.
 #pragma once
 
 #include "mha_common.hpp"
@@ -34,11 +46,12 @@ constexpr int kTopkCand = 4096;  // LDS room for the entries of the threshold bi
 constexpr int kTopkChunkVec = 2048;  // float4 vectors in the first chunk (8192 entries)
 constexpr int kTopkSmallK = 64;      // the wave-sort path: K up to one wave's lanes
 constexpr int kTopkBatchVec = kTopkThreads * kTopkUnroll;  // float4 vectors per batch (16384 entries)
-constexpr int kTopkListCap = 320;    // candidate slots per wave on the wave-sort path
+constexpr int kTopkListCap = 5120;   // candidate slots on the wave-sort path
+constexpr int kTopkRankMax = 256;    // up to this many candidates, selection by rank
 
 // LDS beside the 4096-bin histogram: either the selection and candidate
-// arrays of the paths that read the row twice, or the wave-sort path's 16
-// candidate lists.
+// arrays of the paths that read the row twice, or the wave-sort path's
+// candidate list.
 union TopkLds {
     struct {
         uint32_t sel_key[kTopkMaxK];
@@ -46,10 +59,10 @@ union TopkLds {
         uint32_t cand_key[kTopkCand];
         int32_t cand_idx[kTopkCand];
     } g;
-    uint64_t lists[kTopkThreads / 64][kTopkListCap];
+    uint64_t list[kTopkListCap];
 };
-static_assert(sizeof(uint64_t[kTopkThreads / 64][kTopkListCap]) <= 2 * kTopkMaxK * 4 + 2 * kTopkCand * 4,
-              "the lists share the selection arrays' space");
+static_assert(sizeof(uint64_t[kTopkListCap]) <= 2 * kTopkMaxK * 4 + 2 * kTopkCand * 4,
+              "the list shares the selection arrays' space");
 
 struct TopkParams {
     float *values;
@@ -254,12 +267,38 @@ __device__ inline void lds_bitonic_sort(uint32_t *key, int32_t *idx, int n)
     __syncthreads();
 }
 
+// Candidate list of the wave-sort path, and its length.
+static __shared__ TopkLds lds;
+static __shared__ int list_len;
+
+// Appends the entries among w[0..3] (indices e .. e + 3) that are at or
+// above the bound and lie before `end` to the candidate list: one LDS
+// atomic per element position that any lane has, ballot compaction inside
+// the wave. Every lane of the wave calls it.
+__device__ __forceinline__ void topk_append4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int e, int end,
+                                          bool positive, int lo_bits, uint32_t not_lo)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const bool cand = e + c < end && (positive ? (int)w[c] >= lo_bits : w[c] <= not_lo);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+        if (m) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&list_len, (int)__builtin_popcountll(m));
+            base = __builtin_amdgcn_readfirstlane(base);
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (cand && pos < kTopkListCap) lds.list[pos] = entry_word(w[c], e + c);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
 {
     __shared__ __attribute__((aligned(16))) uint32_t hist[4096];
-    __shared__ TopkLds lds;
     __shared__ int n_cand, n_tie;
-    __shared__ int list_len[kTopkThreads / 64];
     __shared__ uint32_t top_key;
     __shared__ int scratch[kTopkThreads / 64];
     __shared__ int found[2];  // bin, entries still needed within it
@@ -475,45 +514,66 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         __syncthreads();
     };
 
-    // Wave-sort path (K <= 64, rows of 49152 entries or more), one read.
-    // The row streams in batches of 16384 entries (4 float4 per thread),
-    // four batches in flight. Once the first four are in, each thread's
-    // largest of its 64 entries gives 1024 distinct entries; the bin of
-    // their K-th largest key (4096-bin histogram of the top 12 key bits,
-    // searched downward from the top one by one wave) bounds the row's K-th
-    // largest from below. Each wave appends the entries at or above the
-    // bound that it reads to a list of its own in LDS (ballot compaction,
-    // no atomics). The lists, joined, are cut into chunks of 64 that waves
-    // sort in registers, and a tree of bitonic merges between waves leaves
-    // the row's 64 largest, in order, in wave 0. A list that would overflow
-    // sends the row to the paths below.
-    if (K <= kTopkSmallK && nvec >= 4 * kTopkBatchVec) {
+    // One-read path (K <= 64, rows of 81920 entries or more). The row
+    // streams in batches of 16384 entries (4 float4 per thread). Batches 0
+    // to 3 go out at once; once they are in, batch 4 goes out and each
+    // thread's largest of its 64 entries gives 1024 distinct entries: the
+    // bin of their K-th largest key (4096-bin histogram of the top 12 key
+    // bits, searched downward from the top bin by one wave) bounds the
+    // row's K-th largest from below. Then the batches are tested against
+    // the bound as they come, five in flight, and the entries at or above
+    // it join one list in LDS (one LDS atomic per wave and element position
+    // that has any, ballot compaction inside the wave). Selection: by rank
+    // for up to 256 candidates; else chunks of 64 sorted in registers and
+    // a tree of bitonic merges between waves, which leaves the row's 64
+    // largest, in order, in wave 0. A list that would overflow sends the
+    // row to the paths below.
+    if (K <= kTopkSmallK && nvec >= 5 * kTopkBatchVec) {
         const int lane = tid & 63, wave = tid >> 6;
         const int nb = (nvec + kTopkBatchVec - 1) / kTopkBatchVec;
-        // Loads past the row's end read its last vector again (results unused).
+        // The last batch re-reads the row's last vector past its end.
         auto load = [&](int b, float4 (&d)[kTopkUnroll]) {
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u) d[u] = xv[min(b * kTopkBatchVec + u * kTopkThreads + tid, nvec - 1)];
         };
-        float4 r0[kTopkUnroll], r1[kTopkUnroll], r2[kTopkUnroll], r3[kTopkUnroll];
+        float4 r0[kTopkUnroll], r1[kTopkUnroll], r2[kTopkUnroll], r3[kTopkUnroll], r4[kTopkUnroll];
         load(0, r0);
         load(1, r1);
         load(2, r2);
         load(3, r3);
         for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
-        if (tid == 0) top_key = 0u;
+        if (tid == 0) {
+            top_key = 0u;
+            list_len = 0;
+        }
         __syncthreads();
         {
-            // Largest of the thread's 64 entries (all inside the row), as a key.
-            float mx = -INFINITY;
+            // Largest of the thread's 64 entries (all inside the row), as a
+            // key. On the raw bits as signed integers: with any entry of
+            // sign 0 the largest integer is the largest value, else the
+            // smallest integer is (the negative value nearest zero).
+            int imax = INT_MIN, imin = INT_MAX;
             auto fold = [&](const float4 (&d)[kTopkUnroll]) {
 #pragma unroll
-                for (int u = 0; u < kTopkUnroll; ++u) mx = fmaxf(fmaxf(mx, fmaxf(d[u].x, d[u].y)), fmaxf(d[u].z, d[u].w));
+                for (int u = 0; u < kTopkUnroll; ++u) {
+                    const int a = __float_as_int(d[u].x), b = __float_as_int(d[u].y);
+                    const int c = __float_as_int(d[u].z), e = __float_as_int(d[u].w);
+                    imax = max(max(imax, a), b);
+                    imax = max(max(imax, c), e);
+                    imin = min(min(imin, a), b);
+                    imin = min(min(imin, c), e);
+                }
             };
             fold(r0);
             fold(r1);
             fold(r2);
             fold(r3);
+            const float mx = __int_as_float(imax >= 0 ? imax : imin);
+            // Batches 0 to 3 have landed: batch 4 goes out now, so that it
+            // streams in while the bound is found.
+            __builtin_amdgcn_sched_barrier(0);
+            load(4, r4);
+            __builtin_amdgcn_sched_barrier(0);
             const uint32_t key = order_key(mx);
             atomicAdd(&hist[key >> 20], 1u);
             uint32_t wmax = key;
@@ -557,29 +617,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         const bool positive = lo > 0x80000000u;
         const int lo_bits = (int)(lo & 0x7FFFFFFFu);
         const uint32_t not_lo = ~lo;
-        int cnt = 0;  // wave-uniform; above kTopkListCap the list has overflowed
-        auto append = [&](bool cand, uint32_t bits, int idx) {
-            const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
-            if (m) {
-                const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                if (cand && pos < kTopkListCap) lds.lists[wave][pos] = entry_word(bits, idx);
-                cnt += __builtin_popcountll(m);
-            }
-        };
+        // The histogram's space now holds the ranks of the candidates.
+        uint32_t *const rank = hist;
+        if (tid < kTopkRankMax) rank[tid] = 0u;
+        // One test per float4 (the largest, or smallest, of its four words
+        // against the bound); the rare vectors that pass go out of line,
+        // which also drops the re-read copies of the last vector.
         auto process_as = [&](auto pos, int b, const float4 (&d)[kTopkUnroll]) {
+            constexpr bool POS = decltype(pos)::value;
 #pragma unroll
             for (int u = 0; u < kTopkUnroll; ++u) {
-                const int j = b * kTopkBatchVec + u * kTopkThreads + tid;
-                const bool valid = j < nvec;
-                const int e = head + 4 * j;
                 const uint32_t w[4] = {__float_as_uint(d[u].x), __float_as_uint(d[u].y),
                                        __float_as_uint(d[u].z), __float_as_uint(d[u].w)};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bool above = decltype(pos)::value ? (int)w[c] >= lo_bits : w[c] <= not_lo;
-                    append(valid && above, w[c], e + c);
-                }
+                const bool any = POS ? max(max((int)w[0], (int)w[1]), max((int)w[2], (int)w[3])) >= lo_bits
+                                     : min(min(w[0], w[1]), min(w[2], w[3])) <= not_lo;
+                if (__builtin_amdgcn_ballot_w64(any))
+                    topk_append4(w[0], w[1], w[2], w[3], head + 4 * (b * kTopkBatchVec + u * kTopkThreads + tid),
+                                 tail0, POS, lo_bits, not_lo);
             }
         };
         auto process = [&](int b, const float4 (&d)[kTopkUnroll]) {
@@ -588,46 +642,74 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
             else
                 process_as(std::false_type{}, b, d);
         };
-        for (int b = 0; b < nb; b += 4) {
+        for (int b = 0; b < nb; b += 5) {
             process(b, r0);
-            load(b + 4, r0);
+            if (b + 5 < nb) load(b + 5, r0);
             if (b + 1 < nb) process(b + 1, r1);
-            load(b + 5, r1);
+            if (b + 6 < nb) load(b + 6, r1);
             if (b + 2 < nb) process(b + 2, r2);
-            load(b + 6, r2);
+            if (b + 7 < nb) load(b + 7, r2);
             if (b + 3 < nb) process(b + 3, r3);
-            load(b + 7, r3);
+            if (b + 8 < nb) load(b + 8, r3);
+            if (b + 4 < nb) process(b + 4, r4);
+            if (b + 9 < nb) load(b + 9, r4);
         }
-        {
-            const float h = tid < head ? x[tid] : 0.f;
-            append(tid < head && order_key(h) >= lo, __float_as_uint(h), tid);
-            const float t = tail0 + tid < V ? x[tail0 + tid] : 0.f;
-            append(tail0 + tid < V && order_key(t) >= lo, __float_as_uint(t), tail0 + tid);
+        if (head > 0 || tail0 < V) {
+            // The scalar head and tail: 0 .. 3 entries each, one per thread.
+            const int i = tid < head ? tid : tail0 + tid - 4;
+            const bool in = tid < head || (tid >= 4 && i < V);
+            const uint32_t h = in ? __float_as_uint(x[i]) : 0u;
+            if (__builtin_amdgcn_ballot_w64(in))
+                topk_append4(h, 0u, 0u, 0u, in ? i : 0, in ? i + 1 : 0, positive, lo_bits, not_lo);
         }
-        if (lane == 0) list_len[wave] = cnt;
         __syncthreads();
-        int total = 0;
-        bool overflowed = false;
+        const int total = list_len;
+        if (total <= kTopkRankMax) {
+            // Few candidates: each one's rank is the number of larger
+            // ones (the words are distinct), counted by all 16 waves, each
+            // taking one chunk of 64 candidates against one share of the
+            // list; the K of rank below K go straight to their places.
+            // Wave-uniform arithmetic (shifts: 1, 2 or 4 chunks, in 16, 8
+            // or 4 shares).
+            const int uw = __builtin_amdgcn_readfirstlane(wave);
+            const int cshift = total <= 64 ? 0 : total <= 128 ? 1 : 2;
+            const int chunk = uw & ((1 << cshift) - 1), part = uw >> cshift;
+            {
+                const int g = 64 * chunk + lane;
+                const uint64_t mine = g < total ? lds.list[g] : ~0ull;
+                const int share = (total + (15 >> cshift)) >> (4 - cshift);  // ceil(total / parts)
+                const int j0 = min(part * share, total), j1 = min(j0 + share, total);
+                uint32_t larger = 0u;
+                int j = j0;
+                for (; j + 8 <= j1; j += 8) {  // eight broadcast reads in flight
+                    uint64_t o[8];
 #pragma unroll
-        for (int w = 0; w < kTopkThreads / 64; ++w) {
-            total += list_len[w];
-            overflowed |= list_len[w] > kTopkListCap;
+                    for (int u = 0; u < 8; ++u) o[u] = lds.list[j + u];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) larger += o[u] > mine;
+                }
+                for (; j < j1; ++j) larger += lds.list[j] > mine;
+                if (g < total && larger) atomicAdd(&rank[g], larger);
+            }
+            __syncthreads();
+            if (tid < total) {
+                const uint32_t r = rank[tid];
+                if (r < (uint32_t)K) {
+                    const uint64_t wd = lds.list[tid];
+                    p.values[(int64_t)blockIdx.x * K + r] = entry_value(wd);
+                    p.indices[(int64_t)blockIdx.x * K + r] = entry_index(wd);
+                }
+            }
+            return;
         }
-        if (!overflowed) {
-            // The lists, end to end, cut into chunks of 64; wave w sorts
-            // chunks w, w + 16, .. and keeps the 64 largest, descending (0 pads).
+        if (total <= kTopkListCap) {
+            // The list cut into chunks of 64; wave w sorts chunks w, w + 16,
+            // .. and keeps the 64 largest, descending (0 pads).
             const int nchunks = (total + 63) >> 6;
             uint32_t th = 0u, tl = 0u;
             for (int c = wave; c < nchunks; c += kTopkThreads / 64) {
-                const int g = 64 * c + lane;  // position in the joined lists
-                int src = 0, base = 0;        // slot in lds.lists of position g
-#pragma unroll
-                for (int w = 0; w < kTopkThreads / 64; ++w) {
-                    const int n = list_len[w];
-                    if (g >= base && g < base + n) src = w * kTopkListCap + g - base;
-                    base += n;
-                }
-                const uint64_t v = g < total ? (&lds.lists[0][0])[src] : 0ull;
+                const int g = 64 * c + lane;
+                const uint64_t v = g < total ? lds.list[g] : 0ull;
                 uint32_t h = (uint32_t)(v >> 32), l = (uint32_t)v;
                 wave_sort_desc(h, l);
                 if (c == wave) {

@@ -48,13 +48,15 @@ CASES = [
     # threshold bins of more than 4096 entries: the multi-pass path
     (2, 20000, 100, "zeros"),
     (2, 50000, 300, "ties"),
-    # K <= 64 on rows of 49152 entries or more: the wave-sort path (rows
-    # start at every 16-byte phase), and its hand-over to the paths above
-    # when a wave's candidate list overflows (ties, zeros)
+    # K <= 64 on rows of 81920 entries or more: the one-read path (rows
+    # start at every 16-byte phase; up to 256 candidates, selection by
+    # rank), and its hand-over to the paths above when the candidate list
+    # overflows (ties, zeros, huge_tiny)
     (3, 100003, 64, "normal"),
-    (4, 49157, 1, "normal"),
+    (4, 81923, 1, "normal"),
     (2, 131071, 33, "frequencies"),
-    (2, 49153, 33, "zeros"),
+    (2, 200003, 64, "frequencies"),  # about 200 candidates: four chunks ranked
+    (2, 90001, 33, "zeros"),
     (2, 98304, 64, "huge_tiny"),
 ]
 
@@ -68,15 +70,16 @@ def test_topk_matches_oracle(case):
 
 
 def test_topk_negative_rows():
-    """All-negative rows: the wave-sort path's bound is a negative value."""
-    x = inputs.make_scores(3, 70001, "normal", seed=11) - 10.0
+    """All-negative rows: the one-read path's bound is a negative value."""
+    x = inputs.make_scores(3, 100001, "normal", seed=11) - 10.0
     check(x, 50)
 
 
 def test_topk_zeros_among_negatives():
     """A thousand signed zeros among negatives, K = 64: the K-th largest
     is zero, every chosen value ties at zero and the lowest indices win;
-    -0.0 comes back bit for bit."""
+    -0.0 comes back bit for bit. About 1000 candidates: the register
+    sorts and the merge tree."""
     g = torch.Generator("cpu").manual_seed(5)
     x = -(inputs.make_scores(2, 90000, "normal", seed=12).abs() + 1.0)
     for r in range(2):
@@ -87,9 +90,9 @@ def test_topk_zeros_among_negatives():
 
 
 def test_topk_ascending_rows():
-    """Increasing rows: the first batch bounds nothing away, so a wave's
-    list overflows and the row goes to the two-read paths."""
-    x = torch.arange(2 * 60000, dtype=torch.float32).view(2, 60000) / 7.0
+    """Increasing rows: the first batches bound nothing away, so the
+    candidate list overflows and the row goes to the two-read paths."""
+    x = torch.arange(2 * 120000, dtype=torch.float32).view(2, 120000) / 7.0
     check(x, 20)
 
 
