@@ -262,6 +262,20 @@ def test_huge_scale_tiny_inputs(dt, D):
     check(got, want, dt, f"scale 1e38 {dt} D{D}")
 
 
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("mask,window", [("none", -1), ("causal", -1)])
+def test_fp16_scale_above_one_over_log2e(D, mask, window):
+    """fp16 at head dims 32 and 64 with scale * log2(e) > 1: Q is not
+    pre-scaled (a scaled fp16 Q could overflow), so the scale is applied
+    to the fp32 scores."""
+    q, k, v = inputs.make_qkv(1, 300, 4, 2, D, "f16", seed=31 + D)
+    scale = 1.0
+    note(f"fp16 D{D} {mask} scale {scale}")
+    got = run_gpu(q, k, v, scale, mask, window)
+    want = oracle.attention(q, k, v, scale, mask, window)
+    check(got, want, "f16", f"fp16 D{D} {mask} scale 1")
+
+
 def test_peaky_softmax_fp16_small():
     w = inputs.WORKLOADS[4].with_(S=640, H=4, Hkv=4)
     q, k, v = inputs.workload_qkv(w)
