@@ -380,21 +380,25 @@ def time_topk(steps: int, warmup: int, with_cpu: bool):
     vals = torch.empty(w["B"], w["K"], device="cuda")
     idx = torch.empty(w["B"], w["K"], dtype=torch.int32, device="cuda")
     call = lambda: fa.topk(x, w["K"], values=vals, indices=idx)  # noqa: E731
-    t_end = time.perf_counter() + SETTLE_S
-    while time.perf_counter() < t_end:
-        call()
+
+    def per_launch_ms(fn):
+        t_end = time.perf_counter() + SETTLE_S
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for s, e in ev:
-        s.record()
-        call()
-        e.record()
-    torch.cuda.synchronize()
-    ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for s, e in ev:
+            s.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in ev) / steps
+
+    ms = per_launch_ms(call)
     nbytes = w["B"] * w["V"] * 4 + w["B"] * w["K"] * 8
     gbps = nbytes / (ms * 1e-3) / 1e9
     out = {"workload": w["name"], "launch_ms_mean": round(ms, 5),
@@ -402,6 +406,13 @@ def time_topk(steps: int, warmup: int, with_cpu: bool):
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                         "algorithmic_bytes": nbytes}}
+    # Yardsticks, timed the same way: the library top-K on the same rows,
+    # and a plain streaming read of them (a row max), the floor for one read.
+    ms_lib = per_launch_ms(lambda: torch.topk(x, w["K"], dim=1))
+    ms_read = per_launch_ms(lambda: torch.amax(x, dim=1))
+    out["yardsticks"] = {"torch_topk": {"launch_ms_mean": round(ms_lib, 5)},
+                         "torch_row_max_read": {"launch_ms_mean": round(ms_read, 5),
+                                                "gbps": round(w["B"] * w["V"] * 4 / (ms_read * 1e-3) / 1e9, 1)}}
     if with_cpu:
         from oracle import topk as otk
 
