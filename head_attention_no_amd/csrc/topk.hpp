@@ -8,9 +8,9 @@
 // One 1024-thread workgroup (16 waves) per row. Floats map to unsigned
 // order keys (larger float, larger key).
 //
-// K <= 64 on long rows (the sampler's case): one read. Four batches of
-// 16384 entries stream in; each thread's largest entry bounds the row's
-// K-th largest from below (their K-th largest, found with a histogram of
+// K <= 64 on rows of 16384 entries or more (the sampler's case): one
+// read. Up to four full batches of 16384 entries stream in; each thread's
+// largest entry among them bounds the row's K-th largest from below (their K-th largest, found with a histogram of
 // the top 12 key bits), and the rest of the row streams while every entry
 // at or above the bound joins a candidate list in LDS. Up to 256
 // candidates are ranked by counting (all waves share the comparisons);
@@ -514,13 +514,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         __syncthreads();
     };
 
-    // One-read path (K <= 64, rows of 81920 entries or more). The row
+    // One-read path (K <= 64, rows of 16384 entries or more). The row
     // streams in batches of 16384 entries (4 float4 per thread). Batches 0
     // to 3 go out at once; once they are in, batch 4 goes out and each
-    // thread's largest of its 64 entries gives 1024 distinct entries: the
-    // bin of their K-th largest key (4096-bin histogram of the top 12 key
-    // bits, searched downward from the top bin by one wave) bounds the
-    // row's K-th largest from below. Then the batches are tested against
+    // thread's largest entry in the full ones among them (up to 64
+    // entries) gives 1024 distinct entries: the bin of their K-th largest
+    // key (4096-bin histogram of the top 12 key bits, searched downward
+    // from the top bin by one wave) bounds the row's K-th largest from
+    // below. Then the batches are tested against
     // the bound as they come, five in flight, and the entries at or above
     // it join one list in LDS (one LDS atomic per wave and element position
     // that has any, ballot compaction inside the wave). Selection: by rank
@@ -528,9 +529,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     // a tree of bitonic merges between waves, which leaves the row's 64
     // largest, in order, in wave 0. A list that would overflow sends the
     // row to the paths below.
-    if (K <= kTopkSmallK && nvec >= 5 * kTopkBatchVec) {
+    if (K <= kTopkSmallK && nvec >= kTopkBatchVec) {
         const int lane = tid & 63, wave = tid >> 6;
         const int nb = (nvec + kTopkBatchVec - 1) / kTopkBatchVec;
+        const int nfull = nvec / kTopkBatchVec;  // batches without re-read vectors
         // The last batch re-reads the row's last vector past its end.
         auto load = [&](int b, float4 (&d)[kTopkUnroll]) {
 #pragma unroll
@@ -538,9 +540,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         };
         float4 r0[kTopkUnroll], r1[kTopkUnroll], r2[kTopkUnroll], r3[kTopkUnroll], r4[kTopkUnroll];
         load(0, r0);
-        load(1, r1);
-        load(2, r2);
-        load(3, r3);
+        if (nb > 1) load(1, r1);
+        if (nb > 2) load(2, r2);
+        if (nb > 3) load(3, r3);
         for (int i = tid; i < 4096; i += kTopkThreads) hist[i] = 0u;
         if (tid == 0) {
             top_key = 0u;
@@ -548,10 +550,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         }
         __syncthreads();
         {
-            // Largest of the thread's 64 entries (all inside the row), as a
-            // key. On the raw bits as signed integers: with any entry of
-            // sign 0 the largest integer is the largest value, else the
-            // smallest integer is (the negative value nearest zero).
+            // Largest of the thread's entries in the first full batches (up
+            // to four, 16 entries each, all inside the row), as a key. On
+            // the raw bits as signed integers: with any entry of sign 0 the
+            // largest integer is the largest value, else the smallest
+            // integer is (the negative value nearest zero).
             int imax = INT_MIN, imin = INT_MAX;
             auto fold = [&](const float4 (&d)[kTopkUnroll]) {
 #pragma unroll
@@ -565,14 +568,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
                 }
             };
             fold(r0);
-            fold(r1);
-            fold(r2);
-            fold(r3);
+            if (nfull > 1) fold(r1);
+            if (nfull > 2) fold(r2);
+            if (nfull > 3) fold(r3);
             const float mx = __int_as_float(imax >= 0 ? imax : imin);
             // Batches 0 to 3 have landed: batch 4 goes out now, so that it
             // streams in while the bound is found.
             __builtin_amdgcn_sched_barrier(0);
-            load(4, r4);
+            if (nb > 4) load(4, r4);
             __builtin_amdgcn_sched_barrier(0);
             const uint32_t key = order_key(mx);
             atomicAdd(&hist[key >> 20], 1u);

@@ -48,12 +48,16 @@ CASES = [
     # threshold bins of more than 4096 entries: the multi-pass path
     (2, 20000, 100, "zeros"),
     (2, 50000, 300, "ties"),
-    # K <= 64 on rows of 81920 entries or more: the one-read path (rows
-    # start at every 16-byte phase; up to 256 candidates, selection by
-    # rank), and its hand-over to the paths above when the candidate list
+    # K <= 64 on rows of 16384 entries or more: the one-read path (rows
+    # start at every 16-byte phase; the bound from one to four full
+    # batches; up to 256 candidates selected by rank, more by the sort
+    # tree), and its hand-over to the paths above when the candidate list
     # overflows (ties, zeros, huge_tiny)
     (3, 100003, 64, "normal"),
     (4, 81923, 1, "normal"),
+    (3, 16387, 64, "normal"),       # one full batch and a few vectors
+    (2, 32000, 40, "frequencies"),  # one full batch, one partial
+    (2, 65537, 17, "ties"),         # four full batches, no fifth; ~1500 tied candidates
     (2, 131071, 33, "frequencies"),
     (2, 200003, 64, "frequencies"),  # about 200 candidates: four chunks ranked
     (2, 90001, 33, "zeros"),
