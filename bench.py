@@ -159,22 +159,34 @@ def time_gpu(w, steps: int, warmup: int):
     for _ in range(warmup):
         fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
     torch.cuda.synchronize()
+    # The timed steps: one pair of HIP events around them on the kernel's
+    # stream (no event between launches), bracketed by synchronisations.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = e0.elapsed_time(e1)
+    # Spread of single launches (each between two events), after the timed
+    # steps; reported beside the mean, not used for it.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for s, e in ev:
         s.record(stream)
         fa.attention(q, k, v, w.scale, w.mask, w.window, out=out, stream=stream)
         e.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = sorted(s.elapsed_time(e) for s, e in ev)
     return {
         "wall_s": wall,
         "ms_per_step": wall * 1e3 / steps,
-        "launch_ms_mean": sum(launch_ms) / len(launch_ms),
+        "launch_ms_mean": region_ms / steps,
         "launch_ms_median": launch_ms[len(launch_ms) // 2],
         "launch_ms_min": launch_ms[0],
+        "single_launch_ms_mean": sum(launch_ms) / len(launch_ms),
         "clock": clock,
     }
 
@@ -382,6 +394,8 @@ def time_topk(steps: int, warmup: int, with_cpu: bool):
     call = lambda: fa.topk(x, w["K"], values=vals, indices=idx)  # noqa: E731
 
     def per_launch_ms(fn):
+        """Mean per launch over `steps` back-to-back launches between one
+        pair of HIP events (after a settle period and warm-up)."""
         t_end = time.perf_counter() + SETTLE_S
         while time.perf_counter() < t_end:
             fn()
@@ -389,14 +403,13 @@ def time_topk(steps: int, warmup: int, with_cpu: bool):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        for s, e in ev:
-            s.record()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
             fn()
-            e.record()
+        e.record()
         torch.cuda.synchronize()
-        return sum(s.elapsed_time(e) for s, e in ev) / steps
+        return s.elapsed_time(e) / steps
 
     ms = per_launch_ms(call)
     nbytes = w["B"] * w["V"] * 4 + w["B"] * w["K"] * 8
