@@ -362,6 +362,39 @@ def measured_traffic(w):
     return None, None
 
 
+def write_traffic(w, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str):
+    """Writes profiles/<kernel>_<workload>.traffic.json from four rocprofv3
+    --pmc runs (FETCH_SIZE and WRITE_SIZE of the workload's bench run, and of
+    the --copy-calibration 256 run): the last attention dispatch's counters,
+    each scaled by what the same counter reads for the plain 256 MiB copy."""
+    import csv
+
+    def last(d, name_part):
+        with open(os.path.join(d, "pmc_counter_collection.csv")) as fh:
+            rows = [r for r in csv.DictReader(fh) if name_part in r["Kernel_Name"]]
+        did = max(int(r["Dispatch_Id"]) for r in rows)
+        return {r["Counter_Name"]: float(r["Counter_Value"]) for r in rows if int(r["Dispatch_Id"]) == did}
+
+    fetch = last(fetch_dir, "mha_fwd")["FETCH_SIZE"]
+    write = last(write_dir, "mha_fwd")["WRITE_SIZE"]
+    cf = last(copy_fetch_dir, "copyBuffer")["FETCH_SIZE"]
+    cw = last(copy_write_dir, "copyBuffer")["WRITE_SIZE"]
+    fs, ws = 256 * 1024 / cf, 256 * 1024 / cw
+    name = f"mha_fwd16_{w.dtype}_d{w.D}_{w.mask}_{w.name.split('_', 1)[1]}" if w.dtype != "f32" else w.name
+    out = {"kernel_sources_sha256_16": kernel_sources_hash(), "workload": w.name,
+           "fetch_kib": fetch, "write_kib": write, "fetch_scale": fs, "write_scale": ws,
+           "traffic_bytes_per_launch": fetch * 1024 * fs + write * 1024 * ws}
+    path = os.path.join(ROOT, "profiles", f"{TRAFFIC_FILE.get(w.name, name)}.traffic.json")
+    out["source"] = os.path.basename(path).replace(".traffic.json", ".md")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return path, out
+
+
+# Profile file stem per workload (the bench workload's profile name).
+TRAFFIC_FILE = {"gqa_b2_s4096_h32kv8_d128_bf16_causal": "mha_fwd16_bf16_d128_causal_gqa_b2_s4096"}
+
+
 def roofline(w, t):
     fl = flops(w)
     achieved = fl / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -549,7 +582,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead, time a plain device copy of MIB MiB (reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="instead, write profiles/*.traffic.json for --workload from four rocprofv3 "
+                         "--pmc output folders (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        from head_attention_no_amd import inputs as _inputs
+
+        path, out = write_traffic(_inputs.BY_NAME[args.workload], *args.write_traffic)
+        print(path, json.dumps(out))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the kernel needs no "
               "collective, and this build measures a single MI355X.", file=sys.stderr)
