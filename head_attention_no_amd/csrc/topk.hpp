@@ -521,14 +521,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
     // entries) gives 1024 distinct entries: the bin of their K-th largest
     // key (4096-bin histogram of the top 12 key bits, searched downward
     // from the top bin by one wave) bounds the row's K-th largest from
-    // below. Then the batches are tested against
-    // the bound as they come, five in flight, and the entries at or above
-    // it join one list in LDS (one LDS atomic per wave and element position
-    // that has any, ballot compaction inside the wave). Selection: by rank
-    // for up to 256 candidates; else chunks of 64 sorted in registers and
-    // a tree of bitonic merges between waves, which leaves the row's 64
-    // largest, in order, in wave 0. A list that would overflow sends the
-    // row to the paths below.
+    // below. Then the batches are tested against the bound as they come,
+    // five in flight, and the entries at or above it join one list in LDS
+    // (one LDS atomic per wave and element position that has any, ballot
+    // compaction inside the wave). Selection: by rank for up to 256
+    // candidates; else chunks of 64 sorted in registers and a tree of
+    // bitonic merges between waves, which leaves the row's 64 largest, in
+    // order, in wave 0. A list that would overflow sends the row to the
+    // paths below.
     if (K <= kTopkSmallK && nvec >= kTopkBatchVec) {
         const int lane = tid & 63, wave = tid >> 6;
         const int nb = (nvec + kTopkBatchVec - 1) / kTopkBatchVec;
@@ -624,8 +624,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(TopkParams p)
         uint32_t *const rank = hist;
         if (tid < kTopkRankMax) rank[tid] = 0u;
         // One test per float4 (the largest, or smallest, of its four words
-        // against the bound); the rare vectors that pass go out of line,
-        // which also drops the re-read copies of the last vector.
+        // against the bound); the rare vectors that pass are split up by
+        // topk_append4, which also drops the re-read copies of the row's
+        // last vector (their indices lie past the body's end).
         auto process_as = [&](auto pos, int b, const float4 (&d)[kTopkUnroll]) {
             constexpr bool POS = decltype(pos)::value;
 #pragma unroll
