@@ -81,6 +81,13 @@ SMALL = [
     (1, 1000, 8, 1, 128, "bf16", "sliding_window", 200),    # 8 packed, window
     (1, 400, 12, 2, 128, "bf16", "causal", -1),             # 6 per K/V head: 2 packed
     (3, 33, 8, 2, 128, "f16", "none", -1),                  # S below one 64-row tile
+    # group sizes that no packing divides evenly, many batches of tiny S
+    (1, 300, 12, 4, 64, "bf16", "causal", -1),              # 3 query heads per K/V head: no packing
+    (1, 257, 10, 2, 128, "f16", "sliding_window", 33),      # 5 per K/V head
+    (2, 190, 6, 2, 256, "f16", "causal", -1),               # 3 per K/V head at D = 256
+    (16, 7, 8, 2, 64, "bf16", "none", -1),                  # 16 batches of 7 rows
+    (3, 129, 12, 3, 32, "f16", "sliding_window", 64),       # 4 per K/V head at D = 32
+    (2, 75, 6, 3, 64, "f32", "causal", -1),                 # fp32, 2 per K/V head, ragged
 ]
 
 
