@@ -43,6 +43,7 @@ struct Params {
     int group_order;  // 1: items in group order (see block_coord)
     int kv_split;  // 1: fp32 key split (mha_fwd32.hpp): 32-row items, keys split over the waves
     int prescale;  // 1: 16-bit kernel with Q pre-scaled by scale_log2 (mha_fwd16.hpp, D <= 64)
+    int few;       // 1: the few-item layout of the 16-bit kernel at D = 256 (Tile16 in mha_fwd16.hpp)
     int window;    // sliding-window width, clamped to S (a window >= S is causal)
     float scale_log2;  // |scale| * log2(e): exp(scale*s) = exp2(s * scale_log2) for scale >= 0
     uint32_t q_sign;   // sign-bit mask XORed into Q so that scale < 0 becomes |scale|

@@ -58,18 +58,28 @@ namespace fa355 {
 // Word 3 of a raw buffer resource (untyped 32-bit access, range checked).
 constexpr int kRsrcWord3 = 0x00020000;
 
-// Per head dim D: keys per tile BN (S^T tiles and two V steps in flight fit
-// the registers), waves per workgroup NW and waves per SIMD WPE (at D = 256
-// the Q fragments and O^T alone take 192 registers, so one wave per SIMD
-// with the 512-register budget), and the LDS swizzle periods (below).
-template <int D>
+// Per head dim D: keys per tile BN (S^T tiles and the V steps in flight fit
+// the registers), waves per workgroup NW and waves per SIMD WPE, and the LDS
+// swizzle periods (below).
+// D = 256 has two layouts. The default one, like D = 128, runs 8 waves of
+// 32 rows, two per SIMD, with 32-key tiles: the Q fragments and O^T take 192
+// of a wave's 256 registers, and the 16 scores and the operands in flight
+// fit the rest. FEW (chosen by the host for calls with few work items, see
+// layout_of in fa355.hip) runs 4 waves, one per SIMD, with 64-key tiles and
+// the pipelined loop: half the rows per work item, so twice the items, which
+// balances causal calls of under two 256-row items per compute unit; there
+// the compiler keeps S^T and O^T in the accumulation registers and moves
+// O^T out to vector registers on every tile, which the default layout
+// (no accumulation registers) avoids: 6-20 % faster where items suffice.
+template <int D, bool FEW = false>
 struct Tile16 {
-    static constexpr int BN = D == 32 ? 128 : 64;  // keys per tile: 128 at D = 32, else 64
-    static constexpr int NW = D == 256 ? 4 : 8;           // waves per workgroup, 32 query rows each
+    static_assert(!FEW || D == 256, "the few-item layout exists at D = 256 only");
+    static constexpr int BN = D == 32 ? 128 : (D == 256 && !FEW) ? 32 : 64;  // keys per tile
+    static constexpr int NW = FEW ? 4 : 8;           // waves per workgroup, 32 query rows each
     // Waves per SIMD: D = 32 and 64, bound by the vector units and at 120
     // registers (64-key tiles at D = 64), run two workgroups per CU (4 waves
     // per SIMD: 8-20 % faster than 2 at D = 32, 3-7 % at D = 64).
-    static constexpr int WPE = D == 256 ? 1 : D <= 64 ? 4 : 2;
+    static constexpr int WPE = FEW ? 1 : D <= 64 ? 4 : 2;
     static constexpr int NKT = BN / 32;           // 32-key sub-tiles of S^T
     static constexpr int ND = D / 32;             // 32-dim sub-tiles of O^T
     static constexpr int G = 512 / D;             // keys per 1 KiB key group
@@ -81,16 +91,20 @@ struct Tile16 {
     static constexpr int VT = D == 256 ? 2 : 1;   // V read bases per 32-dim sub-tile period
     static constexpr int VH = D == 32 ? 2 : 1;    // V read bases per 8-key half period
     static constexpr int V_AHEAD = 2 * ND <= 8 ? 2 : 1;  // PV k-steps whose V reads are in flight
+    // Plain loop at D = 256: V reads issued per PV MFMA, this many MFMAs
+    // ahead, instead of per k-step (0).
+    static constexpr int V_PAIRS_AHEAD = (D == 256 && !FEW) ? 4 : 0;
     // Software-pipelined key loop (the next tile's S MFMAs interleaved with
     // this tile's softmax, then its PV MFMAs with the next tile's max), in an
-    // issue order fixed at compile time: used at D = 256, where one wave per
-    // SIMD leaves no second wave to hide the softmax (17 % faster there). The
+    // issue order fixed at compile time: used by the few-item layout at
+    // D = 256, where one wave per SIMD leaves no second wave to hide the
+    // softmax (17 % faster there than the plain loop in that layout). The
     // plain loop, with its counted K reads, is as fast or faster at D = 64
     // (level unmasked, 1.6 %-5 % faster causal and windowed), and faster at
     // D = 32 (bound by the vector units) and D = 128 (held at the power cap,
     // where the extra S MFMAs of each wave's last tile cost more than the
     // overlap gains).
-    static constexpr bool PIPELINE = D == 256;
+    static constexpr bool PIPELINE = FEW;
     // The plain loop can walk several work items per workgroup (prefetching
     // the next item's Q rows and first K/V tile); calls use that at D = 64
     // and 128 (walks() in mha_common.hpp).
@@ -170,6 +184,9 @@ __device__ inline void lds_wait(u32x2 (&r)[N])
 #pragma unroll
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
 }
+
+// Make r depend on the last wait (for reads waited for by an earlier lds_wait).
+__device__ inline void lds_tie(u32x2 &r) { asm volatile("" : "+v"(r)); }
 
 // 16-byte LDS read at byte address addr + OFF, as inline asm for the same
 // reason as lds_read_tr16, waited for with lds_wait4().
@@ -257,15 +274,16 @@ __device__ inline WaveItem wave_item(const Params &p, int item, int wave, int c3
     return it;
 }
 
-// Tile16<D>::NW waves per workgroup, 32 query rows each.
-// PRE: the pre-scaled Q (Tile16<D>::PRESCALE) of the plain loop.
-template <typename T, int D, int MASK, bool PRE>
-__global__ __launch_bounds__(64 * Tile16<D>::NW)
-__attribute__((amdgpu_waves_per_eu(Tile16<D>::WPE, Tile16<D>::WPE)))
+// Tile16<D, FEW>::NW waves per workgroup, 32 query rows each.
+// PRE: the pre-scaled Q (Tile16<D>::PRESCALE) of the plain loop; FEW: the
+// few-item layout at D = 256.
+template <typename T, int D, int MASK, bool PRE, bool FEW = false>
+__global__ __launch_bounds__((64 * Tile16<D, FEW>::NW))
+__attribute__((amdgpu_waves_per_eu((Tile16<D, FEW>::WPE), (Tile16<D, FEW>::WPE))))
 void mha_fwd16(Params p)
 {
-    static_assert(!PRE || (Tile16<D>::PRESCALE && !Tile16<D>::PIPELINE), "pre-scaled Q: plain loop, D <= 64");
-    using TL = Tile16<D>;
+    using TL = Tile16<D, FEW>;
+    static_assert(!PRE || (TL::PRESCALE && !TL::PIPELINE), "pre-scaled Q: plain loop, D <= 64");
     constexpr int NW = TL::NW;
     constexpr int NTHREADS = 64 * NW;
     constexpr int NCOPY = TL::GROUPS / NW;  // key groups of K (and of V) each wave copies per tile
@@ -788,29 +806,38 @@ void mha_fwd16(Params p)
                         }
                 }
 
-                // V^T operands: the reads for PV k-steps s .. s+V_AHEAD-1 are in
-                // flight while the exponentials of step s are computed.
+                // V^T operands. By k-step (D <= 128): the reads for PV k-steps
+                // s .. s+V_AHEAD-1 are in flight while the exponentials of step s
+                // are computed. By MFMA (D = 256, where a k-step's 16 reads
+                // would take 32 registers): the two reads of PV MFMA j (k-step
+                // j / ND, 32-dim sub-tile j % ND) are issued VJ MFMAs ahead.
                 const uint32_t v_region = lds_base + stage * TL::STAGE_BYTES + TL::TILE_BYTES;
                 uint32_t v_stage[VT][VH];
 #pragma unroll
                 for (int tb = 0; tb < VT; ++tb)
 #pragma unroll
                     for (int hb = 0; hb < VH; ++hb) v_stage[tb][hb] = v_region + v_addr[tb][hb];
-                u32x2 vr[NPV][NVR];
-                auto issue_v = [&](auto s_tag) {
-                    constexpr int s = decltype(s_tag)::value;
-                    if constexpr (s < NPV) {
-                        static_for<ND>([&](auto t_tag) {
-                            constexpr int t = decltype(t_tag)::value;
-                            constexpr int toff = (t - t % VT) * 64 * G;
-                            constexpr int lo = (16 * s) / G * 1024 + toff;
-                            constexpr int hi = (16 * s + 8 * (1 - 1 % VH)) / G * 1024 + toff;
-                            vr[s][2 * t] = lds_read_tr16<lo>(v_stage[t % VT][0]);
-                            vr[s][2 * t + 1] = lds_read_tr16<hi>(v_stage[t % VT][1 % VH]);
-                        });
+                constexpr int NPM = NPV * ND, VJ = TL::V_PAIRS_AHEAD;
+                u32x2 vr[NPM][2];  // the two reads of PV MFMA j
+                auto issue_pair = [&](auto j_tag) {
+                    constexpr int j = decltype(j_tag)::value;
+                    if constexpr (j < NPM) {
+                        constexpr int s = j / ND, t = j % ND;
+                        constexpr int toff = (t - t % VT) * 64 * G;
+                        constexpr int lo = (16 * s) / G * 1024 + toff;
+                        constexpr int hi = (16 * s + 8 * (1 - 1 % VH)) / G * 1024 + toff;
+                        vr[j][0] = lds_read_tr16<lo>(v_stage[t % VT][0]);
+                        vr[j][1] = lds_read_tr16<hi>(v_stage[t % VT][1 % VH]);
                     }
                 };
-                static_for<V_AHEAD>(issue_v);
+                auto issue_v = [&](auto s_tag) {
+                    constexpr int s = decltype(s_tag)::value;
+                    static_for<ND>([&](auto t_tag) { issue_pair(std::integral_constant<int, s * ND + t_tag>{}); });
+                };
+                if constexpr (VJ > 0)
+                    static_for<VJ>(issue_pair);
+                else
+                    static_for<V_AHEAD>(issue_v);
 
                 // Running max; raised (and O, l rescaled) only when it grows by
                 // more than 2^kRescaleLog2.
@@ -863,14 +890,33 @@ void mha_fwd16(Params p)
                         pb[i] = pack2<T>(e0, e1);
                         l_run = sum2<T>(pb[i], l_run);
                     }
-                    lds_wait<(V_AHEAD > 1 && s + 1 < NPV) ? NVR : 0>(vr[s]);  // step s+1's reads may pend
+                    if constexpr (VJ > 0) {
+                        static_for<ND>([&](auto t_tag) {
+                            constexpr int t = decltype(t_tag)::value, j = s * ND + t;
+                            // Pairs j+1 .. j+VJ-1 (those that exist) may pend.
+                            constexpr int later = (NPM - 1 - j < VJ - 1) ? NPM - 1 - j : VJ - 1;
+                            lds_wait<2 * later>(vr[j]);
+                            const u32x4 a = {vr[j][0][0], vr[j][0][1], vr[j][1][0], vr[j][1][1]};
+                            oacc[t] = mfma16<T>(a, pb, oacc[t]);
+                            issue_pair(std::integral_constant<int, j + VJ>{});
+                        });
+                    } else {
+                        // Step s+1's reads may pend.
+                        constexpr int later = (V_AHEAD > 1 && s + 1 < NPV) ? NVR : 0;
+                        lds_wait<later>(vr[s * ND]);
 #pragma unroll
-                    for (int t = 0; t < ND; ++t) {
-                        const u32x4 a = {vr[s][2 * t][0], vr[s][2 * t][1], vr[s][2 * t + 1][0],
-                                         vr[s][2 * t + 1][1]};
-                        oacc[t] = mfma16<T>(a, pb, oacc[t]);
+                        for (int t = 1; t < ND; ++t) {
+                            lds_tie(vr[s * ND + t][0]);
+                            lds_tie(vr[s * ND + t][1]);
+                        }
+#pragma unroll
+                        for (int t = 0; t < ND; ++t) {
+                            const u32x4 a = {vr[s * ND + t][0][0], vr[s * ND + t][0][1], vr[s * ND + t][1][0],
+                                             vr[s * ND + t][1][1]};
+                            oacc[t] = mfma16<T>(a, pb, oacc[t]);
+                        }
+                        issue_v(std::integral_constant<int, s + V_AHEAD>{});
                     }
-                    issue_v(std::integral_constant<int, s + V_AHEAD>{});
                 });
             }
 

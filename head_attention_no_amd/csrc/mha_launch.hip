@@ -53,10 +53,16 @@ hipError_t launch_one(const Params &p, int n_items, hipStream_t stream)
                                dim3(kThreads32), args, 0, stream);
     } else {
         const void *kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK, false>);
+        int threads = 64 * Tile16<D>::NW;
         if constexpr (Tile16<D>::PRESCALE) {
             if (p.prescale) kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK, true>);
         }
-        constexpr int threads = 64 * Tile16<D>::NW;
+        if constexpr (D == 256) {
+            if (p.few) {
+                kernel = reinterpret_cast<const void *>(&mha_fwd16<T, D, MASK, false, true>);
+                threads = 64 * Tile16<D, true>::NW;
+            }
+        }
         int grid = n_items;
         // A walking call (p.walk, set by the C-ABI layer for short items at
         // D = 128) launches the resident workgroup count rounded down to a

@@ -91,6 +91,15 @@ def test_valid_arguments_reach_the_device_check(over):
     assert call(**over) == fa.ERR_DEVICE
 
 
+def d256_waves(B, S, H, Hkv, mask):
+    """Waves per workgroup of a 16-bit call at D = 256: 8 (32-key tiles)
+    when the 8-wave items number at least 512 under a mask or 256 without
+    one (two or one per compute unit), else 4."""
+    hp = max(x for x in (1, 2, 4, 8) if (H // Hkv) % x == 0)
+    items = -(-S // (32 * 8 // hp)) * B * H // hp
+    return 8 if items >= (256 if mask == "none" else 512) else 4
+
+
 @pytest.mark.parametrize("shape", [
     (2, 4096, 32, 8, 128, fa.BF16, "causal", -1),   # groups split over the 8 XCDs; 4 heads packed; walks
     (4, 2048, 32, 32, 128, fa.BF16, "causal", -1),  # MHA: one head per workgroup; walks
@@ -107,11 +116,15 @@ def test_valid_arguments_reach_the_device_check(over):
     (2, 500, 16, 1, 64, fa.BF16, "none", -1),       # 16 heads per K/V head: 8 packed (one per wave)
     (1, 640, 32, 4, 128, fa.F32, "none", -1),       # 8 heads per K/V head, 4-wave workgroups: 4 packed
     (2, 96, 12, 6, 256, fa.BF16, "none", -1),       # 2 packed at D = 256
+    (2, 4096, 16, 16, 256, fa.BF16, "causal", -1),  # D = 256, 512 causal items: 8-wave layout
+    (4, 1024, 16, 16, 256, fa.F16, "causal", -1),   # 256 causal items: 4-wave layout
+    (2, 2048, 16, 16, 256, fa.BF16, "none", -1),    # 256 unmasked items: 8-wave layout
+    (1, 8192, 16, 4, 256, fa.BF16, "sliding_window", 1024),  # 4 packed, 512 items
 ])
 def test_plan_covers_every_tile_once(shape):
     B, S, H, Hkv, D, dt, mask, window = shape
     pl = fa.plan(B, S, H, Hkv, D, dt, mask, window, with_tiles=True)
-    waves = 4 if dt == fa.F32 or D == 256 else 8
+    waves = 4 if dt == fa.F32 else d256_waves(B, S, H, Hkv, mask) if D == 256 else 8
     hp = max(x for x in (1, 2, 4, 8) if x <= waves and (H // Hkv) % x == 0)
     # fp32 calls with at most 256 items of 32 rows split the keys over the
     # waves of a 32-row, one-head workgroup (head dims up to 64).
@@ -120,7 +133,7 @@ def test_plan_covers_every_tile_once(shape):
         hp, waves = 1, 1
     assert pl["heads_per_workgroup"] == hp
     assert pl["block_m"] == 32 * waves // hp
-    assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 64, 128: 64, 256: 64}[D])
+    assert pl["block_n"] == (32 if dt == fa.F32 else {32: 128, 64: 64, 128: 64, 256: 64 if waves == 4 else 32}[D])
     nq = -(-S // pl["block_m"])
     assert pl["num_workgroups"] == nq * B * H // hp
     tiles = pl["tiles"]

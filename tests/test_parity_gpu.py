@@ -381,10 +381,37 @@ def test_walk_over_many_items_whole_output(case):
     check(got, oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask, window), dt, str(case))
 
 
+D256_DEFAULT = [
+    # Enough 256-row work items (512 under a mask, 256 without) for the
+    # 8-wave layout at D = 256 (32-key tiles, V reads per MFMA).
+    (8, 1024, 16, 16, 256, "bf16", "causal", -1),
+    (4, 2000, 16, 16, 256, "f16", "causal", -1),           # ragged S
+    (2, 2048, 16, 16, 256, "bf16", "none", -1),
+    (4, 2100, 16, 4, 256, "f16", "sliding_window", 200),   # 4 heads per K/V head, ragged
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", D256_DEFAULT, ids=lambda c: "B{}_S{}_H{}kv{}_D{}_{}_{}_W{}".format(*c))
+def test_d256_eight_wave_layout_whole_output(case):
+    B, S, H, Hkv, D, dt, mask, window = case
+    note(f"D=256 8-wave case {case}")
+    pl = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt], mask, window)
+    assert pl["block_n"] == 32 and pl["block_m"] * pl["heads_per_workgroup"] == 256
+    q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + H + D)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+    fa.attention(*_dev(q, k, v), 1.0 / math.sqrt(D), mask, window, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert not torch.isnan(got.float()).any(), "some output element was never written"
+    check(got, oracle.attention(q, k, v, 1.0 / math.sqrt(D), mask, window), dt, str(case))
+
+
 @pytest.mark.parametrize("case", [
     (2, 1100, 32, 8, 128, "bf16", "causal", -1),           # walks: resident grid, several items each
     (1, 700, 16, 16, 64, "f16", "sliding_window", 100),    # walks at D = 64
-    (1, 500, 8, 2, 256, "bf16", "none", -1),                # pipelined loop
+    (1, 500, 8, 2, 256, "bf16", "none", -1),                # few items at D = 256: pipelined loop
+    (2, 2048, 16, 16, 256, "f16", "none", -1),              # D = 256, 8-wave layout
 ])
 def test_graph_replays_match_eager(case):
     """The call captured in a HIP graph (torch.cuda.CUDAGraph) replays to the
