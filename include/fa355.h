@@ -135,7 +135,10 @@ const char *fa355_version(void);
  * fits the kernel's waves), against key tiles of block_n keys. fp32 calls
  * at head dim 32 or 64 whose 32-row items number at most 256 use items of
  * 32 rows of one head, the workgroup's four waves each taking every fourth
- * key tile and merging their partial softmax states exactly at the end. Reports the
+ * key tile and merging their partial softmax states exactly at the end.
+ * 16-bit calls at head dim 256 run 8 waves with 32-key tiles, unless those
+ * items would number fewer than 512 under a mask (256 without one): then 4
+ * waves with 64-key tiles, so twice the items. Reports the
  * number of work items (num_workgroups), whether the call walks them
  * (walk: 0 or 1) and, for each of the first `n` item indices, what it
  * computes: tiles[3*w + 0] = query tile (rows tile*block_m ...
