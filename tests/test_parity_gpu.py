@@ -350,10 +350,10 @@ def test_rows_past_the_end_are_never_used(dt, D, mask):
 
 
 WALK = [
-    # B, S, H, Hkv, D, dtype, mask, window: more work items than the GPU holds
-    # workgroups (one per CU at D = 128, two at D = 32 and 64). At D = 64 and
-    # 128 with short items each workgroup walks several items, the last round
-    # only partly filled; the D = 32 case launches one workgroup per item.
+    # B, S, H, Hkv, D, dtype, mask, window: more work items than compute
+    # units. At D = 64 and 128 with short items each workgroup walks several
+    # items, the last round only partly filled; the D = 32 case launches one
+    # workgroup per item.
     (2, 1100, 32, 8, 128, "bf16", "causal", -1),
     (1, 1100, 64, 8, 128, "bf16", "sliding_window", 200),
     (2, 1037, 32, 8, 128, "f16", "none", -1),
@@ -361,6 +361,7 @@ WALK = [
     (4, 1100, 32, 8, 64, "f16", "causal", -1),    # 576 items on 512 resident workgroups
     (8, 1100, 32, 8, 64, "f16", "causal", -1),    # 1152 items: three rounds
     (2, 1500, 64, 16, 64, "bf16", "sliding_window", 150),
+    (4, 2048, 16, 16, 64, "f16", "causal", -1),    # 512 items fit the resident count: one per CU, two rounds
 ]
 
 
@@ -369,8 +370,10 @@ def test_walk_over_many_items_whole_output(case):
     B, S, H, Hkv, D, dt, mask, window = case
     note(f"walk case {case}")
     pl = fa.plan(B, S, H, Hkv, D, {"bf16": fa.BF16, "f16": fa.F16}[dt], mask, window)
-    per_cu = 2 if D <= 64 else 1  # resident workgroups per CU (D = 32, 64: two)
-    assert pl["num_workgroups"] > per_cu * torch.cuda.get_device_properties(0).multi_processor_count
+    # More items than compute units: D = 128 (one workgroup per CU) walks them
+    # on a resident grid; D = 64 (two per CU) too when they outnumber the
+    # resident count, and otherwise on one workgroup per CU.
+    assert pl["num_workgroups"] > torch.cuda.get_device_properties(0).multi_processor_count
     assert pl["walk"] == (D in (64, 128))
     q, k, v = inputs.make_qkv(B, S, H, Hkv, D, dt, seed=S + H + D)
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
