@@ -451,6 +451,8 @@ def test_graph_replays_match_eager(case):
     (1, 65536, 128, 128, 128, "bf16", "causal", -1),
     # fp32 K and V of 2 GiB each (64 K/V heads), q and out of 4 GiB (128 heads).
     (1, 32768, 128, 64, 256, "f32", "sliding_window", 5000),
+    # D = 256 in the 8-wave layout: q and out of 2 GiB (128 heads), 4096 items.
+    (1, 32768, 128, 32, 256, "bf16", "causal", -1),
 ])
 def test_large_tensors_sampled_rows(case):
     """Tensors at the sizes where offsets outgrow 32 bits; a sample of rows
