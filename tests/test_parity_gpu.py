@@ -391,6 +391,9 @@ D256_DEFAULT = [
     (4, 2000, 16, 16, 256, "f16", "causal", -1),           # ragged S
     (2, 2048, 16, 16, 256, "bf16", "none", -1),
     (4, 2100, 16, 4, 256, "f16", "sliding_window", 200),   # 4 heads per K/V head, ragged
+    (600, 1, 1, 1, 256, "bf16", "causal", -1),             # S = 1: one row per item, 7 waves past the end
+    (1, 33, 512, 512, 256, "f16", "causal", -1),           # one full 32-key tile and a 1-key tail
+    (2, 200, 256, 256, 256, "bf16", "sliding_window", 1),  # window 1: each row sees only itself
 ]
 
 
