@@ -362,6 +362,11 @@ WALK = [
     (8, 1100, 32, 8, 64, "f16", "causal", -1),    # 1152 items: three rounds
     (2, 1500, 64, 16, 64, "bf16", "sliding_window", 150),
     (4, 2048, 16, 16, 64, "f16", "causal", -1),    # 512 items fit the resident count: one per CU, two rounds
+    (1, 2100, 32, 8, 128, "bf16", "sliding_window", 1),   # one-tile items: each row sees only itself
+    (1, 2100, 32, 8, 128, "f16", "sliding_window", 64),   # two-tile items
+    (2, 1025, 32, 8, 128, "bf16", "causal", -1),          # last query tile: one row, one wave wholly past the end
+    (2, 2100, 32, 8, 64, "bf16", "sliding_window", 1),    # D = 64, one-tile items, 528 on 512 resident
+    (5, 1025, 32, 8, 64, "f16", "causal", -1),            # D = 64, 680 items, a one-row last tile
 ]
 
 
